@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the LLM.int8() mixed-precision linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one whole call of the hot path on one batch: outlier detection,
+token quantization, outlier gathers, the int8 GEMM and its epilogue (the
+fp16 outlier product and the fp16 store).  The weight is quantized once
+before timing, as it is at load time.  Inputs are seeded synthetic tensors
+(workloads/), resident in HBM before the timed region starts.
+
+Prints one JSON line.  `value` is the effective throughput 2*T*N*K / time
+of a step, in TOPS.  `roofline` is for the dominant kernel (the GEMM),
+timed with HIP events on the stream the library launches on; `cpu_baseline`
+is the CPU oracle timed on a bounded sample of the same call.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA, published
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "prefill_7b_ffn_up_t4096"
+METRIC = "effective TOPS (2*T*N*K/s) of llm_int8_linear"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--threshold", type=float, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one device copy of known size (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def gemm_traffic(path_src: str):
+    """HBM bytes per GEMM launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    f = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        rec = json.load(fh)
+    sha = hashlib.sha256(open(path_src, "rb").read()).hexdigest()
+    if rec.get("gemm_source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(X, W, w, target_s: float):
+    """The oracle on a bounded sample: detection over all of X (the outlier
+    set needs every row), then quantization, the int8 product and the output
+    for the first R rows, R sized so the run takes about target_s."""
+    import numpy as np
+
+    import oracle
+    Wq, sW = oracle.quantize_weight(W)
+    cores = oracle.num_threads()
+    # grow the sample until one run takes a noticeable time, then size the
+    # final sample for about target_s (the per-row cost dominates by then)
+    rows, dt = 4, 0.0
+    while rows < w.T:
+        t0 = time.perf_counter()
+        oracle.linear_rows(X, Wq, sW, w.threshold, np.arange(rows))
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 8:
+            break
+        rows = min(w.T, rows * 4)
+    rows = int(min(w.T, max(4, rows * target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.linear_rows(X, Wq, sW, w.threshold, np.arange(rows))
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows * w.N * w.K
+    return {
+        "value": round(ops / dt / 1e12, 6),
+        "unit": "TOPS",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"detection over all {w.T} rows of X, then quantization, int8 product "
+                   f"and output for the first {rows} of {w.T} rows ({rows}x{w.K}x{w.N}); "
+                   f"{dt:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer "
+              "runs on a single MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import int8_matmul_amd as li8
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    thr = w.threshold if args.threshold is None else args.threshold
+    T, K, N = w.T, w.K, w.N
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    X_np, W_np, _ = workloads.make(args.workload)
+    X = torch.from_numpy(X_np).to(dev)
+    W = torch.from_numpy(W_np).to(dev)
+    Wq, sW = li8.quantize_weight(W)
+    ws = li8.new_workspace(T, K, N, dev)
+    Y = torch.empty((T, N), dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        li8.linear(X, Wq, sW, thr, out=Y, workspace=ws)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        li8.prepare(X, Wq, thr, ws)
+        e1.record()
+        li8.gemm(Wq, sW, T, ws, out=Y)
+        e2.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    prep_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    gemm_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+
+    st = li8.export_stages(ws, T, K, N)
+    nO = int(st["n_outliers"].cpu()[0])
+    nO16 = (nO + 15) // 16 * 16
+    ops = 2.0 * T * N * K
+    tops = ops / (ms_step * 1e-3) / 1e12
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    # algorithmic bytes of the prepare stage: detection reads X; quantization
+    # reads X, writes Xq, sX and the gathered outlier columns of X; the weight
+    # gather reads and writes nO16 bytes per weight row
+    prep_bytes = 2 * T * K + 2 * T * K + T * K + 4 * T + 2 * T * nO16 + 2 * N * nO16
+    prep_gbps = prep_bytes / (prep_ms * 1e-3) / 1e9
+
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    src = os.path.join(ROOT, "int8_matmul_amd", "csrc", "gemm.hip")
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.desc, "name": args.workload, "T": T, "K": K, "N": N,
+                   "threshold": thr, "n_outliers": nO, "parallelism": "single GPU"},
+        "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "prepare_us": round(prep_ms * 1e3, 2),
+        "gemm_us": round(gemm_ms * 1e3, 2),
+        "quant_gbps": round(prep_gbps, 1),
+        "quant_pct_hbm_peak": round(100.0 * prep_gbps / PEAK_HBM_GBPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k_gemm (int8 MFMA GEMM + dequant/outlier epilogue)",
+            "achieved": round(gemm_tops, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOP/s",
+            "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+            "traffic": gemm_traffic(src),
+        },
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(X_np, W_np, w, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

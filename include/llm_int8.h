@@ -1,0 +1,160 @@
+/*
+ * llm_int8.h - C ABI of the LLM.int8() mixed-precision linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer computes Y = X . W^T for fp16 activations X[T,K] and a weight
+ * W[N,K] that has been quantized once to int8 with one scale per output
+ * feature.  Each call:
+ *   1. finds the outlier feature columns of X: columns j in which some
+ *      |X[t,j]| > threshold (the pages use 6.0)
+ *        -- hncyxsy.com/news/230290 (LLM quantization, part 2), section 2.1;
+ *           lowentro.cn "model quantization" notes, Q4;
+ *   2. quantizes every token row of X over its normal columns with a
+ *      symmetric absmax scale, sX[t] = max|x| / 127, code round(x / sX[t])
+ *      clipped to [-127, 127]; outlier columns get code 0
+ *        -- notes Q2 (symmetric formulas) and Q11 (range); tqpw.cn/news/5683,
+ *           section 2.1 (scale = max/127, round, clip);
+ *   3. multiplies the int8 codes, int8 x int8 -> int32, and dequantizes with
+ *      acc * sX[t] * sW[n];
+ *   4. multiplies the outlier columns of X (fp16) with the same columns of
+ *      the dequantized weight in floating point and adds the two parts; the
+ *      sum is stored as fp16
+ *        -- hncyxsy.com/news/230290, section 2.1; tqpw.cn/news/5683,
+ *           section 3.1.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense row-major, in device memory owned by the caller.
+ *     fp16 tensors are passed as raw IEEE binary16 bit patterns (void*).
+ *     Pointers must be 16-byte aligned.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *     the default stream).  No entry point synchronizes, allocates or frees
+ *     device memory, or copies anything to the host.  The library keeps no
+ *     mutable global state: calls on different streams with different
+ *     workspaces may overlap.
+ *   - Validation happens on the host, before anything is launched; a
+ *     non-LI8_OK status means nothing was enqueued, except LI8_ERR_HIP,
+ *     which reports a launch failure.  Device-side faults surface at the
+ *     caller's next synchronization.
+ *   - Shapes: T >= 0 tokens, N >= 0 output features, K >= 0 features with
+ *     K a multiple of 16 and K <= 133144 (so that the int32 sum of K
+ *     products of magnitude <= 127*127 cannot overflow).  T == 0 or N == 0
+ *     is an empty call that enqueues nothing.
+ *   - Inputs must be finite; NaN or Inf in X or W is outside the contract.
+ */
+#ifndef LLM_INT8_H
+#define LLM_INT8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum li8_status {
+    LI8_OK = 0,
+    LI8_ERR_INVALID_ARG = 1, /* null pointer, NaN or negative threshold     */
+    LI8_ERR_SHAPE = 2,       /* negative dim, K % 16 != 0, K > 133144, or a
+                                byte size that overflows int64             */
+    LI8_ERR_ALIGN = 3,       /* a pointer not 16-byte aligned               */
+    LI8_ERR_WORKSPACE = 4,   /* workspace null or smaller than required     */
+    LI8_ERR_HIP = 5          /* a HIP launch or copy failed to enqueue (for
+                                example: no gfx950 code for this device)   */
+} li8_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *li8_status_str(li8_status status);
+
+/*
+ * Vector-wise weight quantization, done once per weight, off the per-call
+ * path (tqpw.cn/news/5683, section 2.1; hncyxsy.com/news/230290, section
+ * 2.1: one scale per output feature; notes Q3: per-channel scales).
+ *   W   [N,K] fp16, read only.
+ *   Wq  [N,K] int8 out:  Wq[n,k] = clamp(rne(fl32(W[n,k] / sW[n])), -127, 127)
+ *   sW  [N]  fp32 out:   sW[n]   = fl32(max_k |W[n,k]| / 127)
+ *   (rne: round half to even; fl32: IEEE fp32 rounding; a row of zeros gets
+ *   sW = 0 and codes 0.)
+ */
+li8_status int8_quantize_weight(const void *W, int64_t N, int64_t K,
+                                int8_t *Wq, float *sW, hipStream_t stream);
+
+/*
+ * Bytes of device workspace that llm_int8_linear and llm_int8_prepare need
+ * for this shape.  It covers the worst case, every column an outlier, so
+ * the size never depends on the data.  Returns 0 if the shape is invalid.
+ */
+size_t llm_int8_workspace_bytes(int64_t T, int64_t K, int64_t N);
+
+/*
+ * The whole layer: Y[T,N] = decomposed X[T,K] . W^T.
+ *   X          [T,K] fp16, read only.
+ *   Wq, sW     the outputs of int8_quantize_weight for W[N,K], read only.
+ *   threshold  outlier threshold, >= 0; +inf disables the decomposition (the
+ *              pure vector-wise int8 product); 0 makes every column that has
+ *              a non-zero value an outlier.
+ *   Y          [T,N] fp16 out, fully overwritten; must not alias an input.
+ *   workspace  device buffer of at least llm_int8_workspace_bytes(T,K,N)
+ *              bytes, owned by the caller; its contents on entry do not
+ *              matter.  Two calls in flight at once need two workspaces.
+ * Equivalent to llm_int8_prepare followed by llm_int8_gemm on the same
+ * stream and workspace.
+ */
+li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW,
+                           float threshold, int64_t T, int64_t K, int64_t N,
+                           void *Y, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * First half of llm_int8_linear (steps 1-2 above): outlier detection,
+ * token-wise quantization of X, and the gathering of the outlier columns of
+ * X and of Wq into compact matrices.  Everything it produces stays in
+ * `workspace`, which llm_int8_gemm then consumes.  Arguments as for
+ * llm_int8_linear.
+ */
+li8_status llm_int8_prepare(const void *X, const int8_t *Wq, float threshold,
+                            int64_t T, int64_t K, int64_t N,
+                            void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * Second half of llm_int8_linear (steps 3-4): the int8 GEMM with its
+ * dequantizing epilogue and the outlier product.  `workspace` must hold
+ * the result of llm_int8_prepare for the same X, Wq, T, K, N, enqueued
+ * earlier on the same stream (or otherwise ordered before this call).
+ *   acc  optional [T,N] int32 out (NULL to skip): the exact int8 sums
+ *        acc[t,n] = sum_j Xq[t,j] * Wq[n,j], stored by the same kernel that
+ *        computes Y (a test hook; it costs 4*T*N bytes of writes).
+ */
+li8_status llm_int8_gemm(const int8_t *Wq, const float *sW,
+                         int64_t T, int64_t K, int64_t N, void *Y,
+                         int32_t *acc, const void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Copies the intermediate results of the last llm_int8_prepare on
+ * `workspace` into caller buffers (device-to-device, on `stream`).  A test
+ * hook: the product path never needs it.  Any output pointer may be NULL.
+ *   outlier_bits [ceil(K/32)] uint32: bit (j % 32) of word j / 32 set iff
+ *                column j is an outlier.
+ *   n_outliers   [1] int32: number of outlier columns nO.
+ *   outlier_idx  [K] int32: the outlier columns in ascending order; entries
+ *                from nO on are unspecified.
+ *   Xq           [T,K] int8: token codes (0 in outlier columns).
+ *   sX           [T] fp32: token scales.
+ *   X_out        [T,K] fp16: X_out[t,i] = X[t, outlier_idx[i]] for i < nO;
+ *                columns nO .. round_up(nO,16)-1 are zero; the rest is
+ *                unspecified.
+ */
+li8_status llm_int8_export_stages(const void *workspace, size_t workspace_bytes,
+                                  int64_t T, int64_t K, int64_t N,
+                                  uint32_t *outlier_bits, int32_t *n_outliers,
+                                  int32_t *outlier_idx, int8_t *Xq, float *sX,
+                                  void *X_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLM_INT8_H */

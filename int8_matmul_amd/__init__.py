@@ -1,0 +1,225 @@
+"""LLM.int8() mixed-precision linear layer for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of ``libllm_int8.so`` (HIP kernels + C ABI, declared
+in ``include/llm_int8.h``).  This module only marshals arguments: every step
+of the computation runs in the library's kernels.  PyTorch provides the
+device memory and the stream; calls are enqueued on torch's current stream
+of the tensors' device and never synchronize.
+
+    Wq, sW = quantize_weight(W)            # once per weight, W fp16 [N,K]
+    Y = linear(X, Wq, sW, threshold=6.0)   # X fp16 [T,K] -> Y fp16 [T,N]
+
+The method (hncyxsy.com/news/230290 "LLM quantization, part 2", section
+2.1; lowentro.cn "model quantization" notes, Q4; tqpw.cn/news/5683,
+sections 2.1 and 3.1): feature columns of X with some |x| > threshold are
+outliers and are multiplied in floating point; the other columns are
+quantized to int8 with a per-token absmax scale (the weight with a
+per-output-feature scale), multiplied as int8 x int8 -> int32, dequantized,
+and added to the outlier product; the result is fp16.
+
+If the library has not been built, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "Int8MatmulError", "LibraryNotBuilt", "library_path", "load_library",
+    "quantize_weight", "workspace_bytes", "new_workspace", "linear", "prepare",
+    "gemm", "export_stages", "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libllm_int8.so")
+_lib = None
+
+STATUS = {
+    0: "LI8_OK",
+    1: "LI8_ERR_INVALID_ARG",
+    2: "LI8_ERR_SHAPE",
+    3: "LI8_ERR_ALIGN",
+    4: "LI8_ERR_WORKSPACE",
+    5: "LI8_ERR_HIP",
+}
+
+
+class Int8MatmulError(RuntimeError):
+    """A library call returned a status other than LI8_OK."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+class LibraryNotBuilt(ImportError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libllm_int8.so (raises LibraryNotBuilt if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise LibraryNotBuilt(
+            f"{_LIB_PATH} is missing; build it with `python -m int8_matmul_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    L.li8_status_str.restype = ctypes.c_char_p
+    L.li8_status_str.argtypes = [ctypes.c_int]
+    L.int8_quantize_weight.restype = ctypes.c_int
+    L.int8_quantize_weight.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.llm_int8_workspace_bytes.restype = sz
+    L.llm_int8_workspace_bytes.argtypes = [i64, i64, i64]
+    L.llm_int8_linear.restype = ctypes.c_int
+    L.llm_int8_linear.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp, sz, vp]
+    L.llm_int8_prepare.restype = ctypes.c_int
+    L.llm_int8_prepare.argtypes = [vp, vp, ctypes.c_float, i64, i64, i64, vp, sz, vp]
+    L.llm_int8_gemm.restype = ctypes.c_int
+    L.llm_int8_gemm.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    L.llm_int8_export_stages.restype = ctypes.c_int
+    L.llm_int8_export_stages.argtypes = [vp, sz, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Int8MatmulError(fn, status)
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _require(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize_weight(W: torch.Tensor, Wq: torch.Tensor | None = None,
+                    sW: torch.Tensor | None = None):
+    """Vector-wise int8 quantization of W fp16 [N,K]: (Wq int8 [N,K], sW fp32 [N])."""
+    L = load_library()
+    _require(W, torch.float16, "W", 2)
+    N, K = W.shape
+    if Wq is None:
+        Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    if sW is None:
+        sW = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check("int8_quantize_weight",
+           L.int8_quantize_weight(_ptr(W), N, K, _ptr(Wq), _ptr(sW), _stream(W.device)))
+    return Wq, sW
+
+
+def workspace_bytes(T: int, K: int, N: int) -> int:
+    n = load_library().llm_int8_workspace_bytes(T, K, N)
+    if n == 0:
+        raise Int8MatmulError("llm_int8_workspace_bytes", 2)
+    return int(n)
+
+
+def new_workspace(T: int, K: int, N: int, device) -> torch.Tensor:
+    return torch.empty(workspace_bytes(T, K, N), dtype=torch.uint8, device=device)
+
+
+def _ws(workspace, T, K, N, device):
+    if workspace is None:
+        workspace = new_workspace(T, K, N, device)
+    _require(workspace, torch.uint8, "workspace", 1)
+    return workspace
+
+
+def linear(X: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, threshold: float = 6.0,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Y fp16 [T,N] = the LLM.int8() decomposed product of X fp16 [T,K] and W."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(sW, torch.float32, "sW", 1)
+    T, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or sW.shape[0] != N:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, sW {tuple(sW.shape)}")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    _require(out, torch.float16, "out", 2)
+    ws = _ws(workspace, T, K, N, X.device)
+    _check("llm_int8_linear",
+           L.llm_int8_linear(_ptr(X), _ptr(Wq), _ptr(sW), float(threshold), T, K, N,
+                             _ptr(out), _ptr(ws), ws.numel(), _stream(X.device)))
+    return out
+
+
+def prepare(X: torch.Tensor, Wq: torch.Tensor, threshold: float, workspace: torch.Tensor):
+    """Detection, token quantization and outlier gathers into `workspace`."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(Wq, torch.int8, "Wq", 2)
+    T, K = X.shape
+    N = Wq.shape[0]
+    ws = _ws(workspace, T, K, N, X.device)
+    _check("llm_int8_prepare",
+           L.llm_int8_prepare(_ptr(X), _ptr(Wq), float(threshold), T, K, N, _ptr(ws),
+                              ws.numel(), _stream(X.device)))
+    return ws
+
+
+def gemm(Wq: torch.Tensor, sW: torch.Tensor, T: int, workspace: torch.Tensor,
+         out: torch.Tensor | None = None, acc: torch.Tensor | None = None):
+    """int8 GEMM + epilogue reading what `prepare` left in `workspace`."""
+    L = load_library()
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(sW, torch.float32, "sW", 1)
+    N, K = Wq.shape
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=Wq.device)
+    _require(out, torch.float16, "out", 2)
+    if acc is not None:
+        _require(acc, torch.int32, "acc", 2)
+    _require(workspace, torch.uint8, "workspace", 1)
+    _check("llm_int8_gemm",
+           L.llm_int8_gemm(_ptr(Wq), _ptr(sW), T, K, N, _ptr(out), _ptr(acc), _ptr(workspace),
+                           workspace.numel(), _stream(Wq.device)))
+    return out
+
+
+def export_stages(workspace: torch.Tensor, T: int, K: int, N: int) -> dict:
+    """Device copies of the intermediate results of the last `prepare`."""
+    L = load_library()
+    _require(workspace, torch.uint8, "workspace", 1)
+    dev = workspace.device
+    nw = max((K + 31) // 32, 1)
+    r = dict(
+        outlier_bits=torch.empty(nw, dtype=torch.int32, device=dev),
+        n_outliers=torch.empty(1, dtype=torch.int32, device=dev),
+        outlier_idx=torch.empty(max(K, 1), dtype=torch.int32, device=dev),
+        Xq=torch.empty((T, K), dtype=torch.int8, device=dev),
+        sX=torch.empty(max(T, 1), dtype=torch.float32, device=dev),
+        X_out=torch.empty((T, K), dtype=torch.float16, device=dev),
+    )
+    _check("llm_int8_export_stages",
+           L.llm_int8_export_stages(_ptr(workspace), workspace.numel(), T, K, N,
+                                    _ptr(r["outlier_bits"]), _ptr(r["n_outliers"]),
+                                    _ptr(r["outlier_idx"]), _ptr(r["Xq"]), _ptr(r["sX"]),
+                                    _ptr(r["X_out"]), _stream(dev)))
+    return r

@@ -1,0 +1,215 @@
+// Host side of the C ABI declared in include/llm_int8.h: argument checks,
+// workspace carving and kernel launches.  No allocation, no host sync.
+#include <math.h>
+#include <string.h>
+
+#include "li8_internal.h"
+#include "llm_int8.h"
+
+using namespace li8;
+
+namespace {
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+li8_status check_shape(int64_t T, int64_t K, int64_t N)
+{
+    if (T < 0 || K < 0 || N < 0)
+        return LI8_ERR_SHAPE;
+    if (K % 16 != 0 || K > kMaxK)
+        return LI8_ERR_SHAPE;
+    // kernels index rows and columns with int; byte offsets are int64
+    const int64_t lim = (int64_t)1 << 31;
+    if (T >= lim || N >= lim)
+        return LI8_ERR_SHAPE;
+    // T*N*4 (acc), T*K*2 and N*K must fit comfortably in int64
+    if ((double)T * (double)N * 4.0 > 9.0e18 || (double)T * (double)K * 3.0 > 9.0e18 ||
+        (double)N * (double)K > 9.0e18)
+        return LI8_ERR_SHAPE;
+    return LI8_OK;
+}
+
+// Exact value of a binary16 magnitude pattern (0 <= m <= 0x7c00).
+double half_mag_value(uint32_t m)
+{
+    const uint32_t e = m >> 10, f = m & 0x3ffu;
+    if (e == 0)
+        return ldexp((double)f, -24);
+    if (e == 31)
+        return INFINITY;
+    return ldexp((double)(f | 0x400u), (int)e - 25);
+}
+
+// Largest binary16 magnitude pattern H whose value is <= thr (thr >= 0),
+// so that |x| > thr  <=>  (bits(x) & 0x7fff) > H for finite x.
+uint16_t threshold_magnitude(float thr)
+{
+    uint32_t lo = 0, hi = 0x7c00;   // value(lo) = 0 <= thr always
+    if (half_mag_value(hi) <= (double)thr)
+        return (uint16_t)hi;        // thr = +inf: nothing finite exceeds it
+    while (hi - lo > 1) {           // invariant: value(lo) <= thr < value(hi)
+        const uint32_t mid = (lo + hi) / 2;
+        if (half_mag_value(mid) <= (double)thr)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return (uint16_t)lo;
+}
+
+li8_status from_hip(hipError_t e) { return e == hipSuccess ? LI8_OK : LI8_ERR_HIP; }
+
+li8_status check_linear_args(const void *X, const int8_t *Wq, float threshold, int64_t T,
+                             int64_t K, int64_t N, const void *ws, size_t ws_bytes)
+{
+    li8_status st = check_shape(T, K, N);
+    if (st != LI8_OK)
+        return st;
+    if (isnan(threshold) || threshold < 0.0f)
+        return LI8_ERR_INVALID_ARG;
+    if (T == 0 || N == 0)
+        return LI8_OK;
+    if (K > 0 && (!X || !Wq))   // with K == 0, X and Wq hold no element
+        return LI8_ERR_INVALID_ARG;
+    if (misaligned(X) || misaligned(Wq))
+        return LI8_ERR_ALIGN;
+    if (!ws || misaligned(ws) || ws_bytes < ws_layout(T, K, N).total)
+        return ws && misaligned(ws) ? LI8_ERR_ALIGN : LI8_ERR_WORKSPACE;
+    return LI8_OK;
+}
+
+li8_status check_gemm_args(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
+                           const void *Y, const int32_t *acc, const void *ws, size_t ws_bytes)
+{
+    li8_status st = check_shape(T, K, N);
+    if (st != LI8_OK)
+        return st;
+    if (T == 0 || N == 0)
+        return LI8_OK;
+    if ((K > 0 && !Wq) || !sW || !Y)
+        return LI8_ERR_INVALID_ARG;
+    if (misaligned(Wq) || misaligned(sW) || misaligned(Y) || (acc && misaligned(acc)))
+        return LI8_ERR_ALIGN;
+    if (!ws || misaligned(ws) || ws_bytes < ws_layout(T, K, N).total)
+        return ws && misaligned(ws) ? LI8_ERR_ALIGN : LI8_ERR_WORKSPACE;
+    return LI8_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *li8_status_str(li8_status s)
+{
+    switch (s) {
+    case LI8_OK: return "LI8_OK";
+    case LI8_ERR_INVALID_ARG: return "LI8_ERR_INVALID_ARG";
+    case LI8_ERR_SHAPE: return "LI8_ERR_SHAPE";
+    case LI8_ERR_ALIGN: return "LI8_ERR_ALIGN";
+    case LI8_ERR_WORKSPACE: return "LI8_ERR_WORKSPACE";
+    case LI8_ERR_HIP: return "LI8_ERR_HIP";
+    }
+    return "LI8_UNKNOWN_STATUS";
+}
+
+li8_status int8_quantize_weight(const void *W, int64_t N, int64_t K, int8_t *Wq, float *sW,
+                                hipStream_t stream)
+{
+    li8_status st = check_shape(1, K, N);
+    if (st != LI8_OK)
+        return st;
+    if (N == 0)
+        return LI8_OK;
+    if (!W || !Wq || !sW)
+        return LI8_ERR_INVALID_ARG;
+    if (misaligned(W) || misaligned(Wq) || misaligned(sW))
+        return LI8_ERR_ALIGN;
+    return from_hip(launch_quantize_weight(static_cast<const uint16_t *>(W), N, K, Wq, sW,
+                                           stream));
+}
+
+size_t llm_int8_workspace_bytes(int64_t T, int64_t K, int64_t N)
+{
+    if (check_shape(T, K, N) != LI8_OK)
+        return 0;
+    return ws_layout(T, K, N).total;
+}
+
+li8_status llm_int8_prepare(const void *X, const int8_t *Wq, float threshold, int64_t T,
+                            int64_t K, int64_t N, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream)
+{
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    const WsLayout L = ws_layout(T, K, N);
+    return from_hip(launch_prepare(static_cast<const uint16_t *>(X), Wq,
+                                   threshold_magnitude(threshold), T, K, N,
+                                   static_cast<char *>(workspace), L, stream));
+}
+
+li8_status llm_int8_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
+                         void *Y, int32_t *acc, const void *workspace, size_t workspace_bytes,
+                         hipStream_t stream)
+{
+    li8_status st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    const WsLayout L = ws_layout(T, K, N);
+    return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), acc,
+                                static_cast<const char *>(workspace), L, stream));
+}
+
+li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW, float threshold,
+                           int64_t T, int64_t K, int64_t N, void *Y, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream)
+{
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    if (st == LI8_OK)
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    const WsLayout L = ws_layout(T, K, N);
+    hipError_t e = launch_prepare(static_cast<const uint16_t *>(X), Wq,
+                                  threshold_magnitude(threshold), T, K, N,
+                                  static_cast<char *>(workspace), L, stream);
+    if (e != hipSuccess)
+        return LI8_ERR_HIP;
+    return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), nullptr,
+                                static_cast<const char *>(workspace), L, stream));
+}
+
+li8_status llm_int8_export_stages(const void *workspace, size_t workspace_bytes, int64_t T,
+                                  int64_t K, int64_t N, uint32_t *outlier_bits,
+                                  int32_t *n_outliers, int32_t *outlier_idx, int8_t *Xq,
+                                  float *sX, void *X_out, hipStream_t stream)
+{
+    li8_status st = check_shape(T, K, N);
+    if (st != LI8_OK)
+        return st;
+    const WsLayout L = ws_layout(T, K, N);
+    if (!workspace || workspace_bytes < L.total)
+        return LI8_ERR_WORKSPACE;
+    const char *ws = static_cast<const char *>(workspace);
+    struct {
+        void *dst;
+        size_t off, bytes;
+    } cp[] = {
+        {outlier_bits, L.bits, 4 * (size_t)((K + 31) / 32)},
+        {n_outliers, L.meta, 4},
+        {outlier_idx, L.idx, 4 * (size_t)K},
+        {Xq, L.Xq, (size_t)T * (size_t)K},
+        {sX, L.sX, 4 * (size_t)T},
+        {X_out, L.XO, 2 * (size_t)T * (size_t)K},
+    };
+    for (auto &c : cp) {
+        if (!c.dst || c.bytes == 0)
+            continue;
+        hipError_t e = hipMemcpyAsync(c.dst, ws + c.off, c.bytes, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess)
+            return LI8_ERR_HIP;
+    }
+    return LI8_OK;
+}
+
+} // extern "C"

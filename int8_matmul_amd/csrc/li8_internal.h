@@ -1,0 +1,60 @@
+// Internal declarations shared by the HIP sources of libllm_int8.so.
+// Not part of the public ABI (include/llm_int8.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace li8 {
+
+// Largest K for which sum_{j<K} |q_x q_w| <= K * 127 * 127 fits in int32.
+constexpr int64_t kMaxK = 133144;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Device workspace carved into fixed regions.  Offsets depend only on the
+// shape (T, K, N), never on the data, so the host needs no readback.
+//   bits : uint32[ceil(K/32)]  outlier column bit set (cleared every call)
+//   meta : int32[64]           meta[0] = nO
+//   idx  : int32[K]            outlier columns, ascending
+//   sX   : fp32[T]             token scales
+//   Xq   : int8[T,K]           token codes, 0 in outlier columns
+//   XO   : fp16[T,K]           X[t, idx[i]] at column i < nO, zero pad to a
+//                              multiple of 16; row stride K
+//   WO   : int8[N,K]           Wq[n, idx[i]] at column i < nO, zero pad to a
+//                              multiple of 16; row stride K
+struct WsLayout {
+    size_t bits, meta, idx, sX, Xq, XO, WO, total;
+};
+
+inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
+{
+    const size_t A = 256;
+    WsLayout L;
+    size_t off = 0;
+    size_t nwords = (size_t)((K + 31) / 32);
+    L.bits = off; off = align_up(off + 4 * (nwords ? nwords : 1), A);
+    L.meta = off; off = align_up(off + 256, A);
+    L.idx = off;  off = align_up(off + 4 * (size_t)(K ? K : 1), A);
+    L.sX = off;   off = align_up(off + 4 * (size_t)(T ? T : 1), A);
+    L.Xq = off;   off = align_up(off + (size_t)T * (size_t)K + 16, A);
+    L.XO = off;   off = align_up(off + 2 * (size_t)T * (size_t)K + 16, A);
+    L.WO = off;   off = align_up(off + (size_t)N * (size_t)K + 16, A);
+    L.total = off;
+    return L;
+}
+
+// Launchers (quant.hip).  All asynchronous on `s`; return hipGetLastError().
+hipError_t launch_quantize_weight(const uint16_t *W, int64_t N, int64_t K,
+                                  int8_t *Wq, float *sW, hipStream_t s);
+hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, uint16_t thr_mag,
+                          int64_t T, int64_t K, int64_t N, char *ws,
+                          const WsLayout &L, hipStream_t s);
+
+// Launcher (gemm.hip).
+hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K,
+                       int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
+                       const WsLayout &L, hipStream_t s);
+
+} // namespace li8

@@ -1,0 +1,397 @@
+// Outlier detection and vector-wise int8 quantization kernels for gfx950.
+//
+// The method (hncyxsy.com/news/230290 "LLM quantization, part 2", section
+// 2.1; lowentro.cn "model quantization" notes, Q2-Q4, Q11; tqpw.cn/news/5683,
+// section 2.1):
+//   outlier columns  O = { j : some |X[t,j]| > threshold }
+//   token scale      sX[t] = max_{j not in O} |X[t,j]| / 127
+//   token codes      Xq[t,j] = round(X[t,j] / sX[t]) clipped to [-127,127],
+//                    0 for j in O
+//   weight scale     sW[n] = max_k |W[n,k]| / 127, codes likewise.
+// Scales are fp32 (IEEE division), codes round half to even.
+//
+// All three kernels are HBM-bound streaming passes: 16-byte coalesced
+// loads, the row or column-strip reduction kept in registers, wave-level
+// reductions, and a single atomic per 32 columns for the outlier bit set.
+//
+// Magnitudes are compared as integers: for a finite binary16 value h,
+// |h| is monotone in (h & 0x7fff), so |x| > thr  <=>  (h & 0x7fff) > H,
+// with H the largest binary16 magnitude pattern whose value is <= thr
+// (computed on the host).  The same ordering gives the exact absmax.
+#include "li8_internal.h"
+
+namespace li8 {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float h2f(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Code of one value for a row scale s (s == 0 means the row is all zero).
+__device__ __forceinline__ int code_of(uint32_t h, float s)
+{
+    if (s == 0.0f)
+        return 0;
+    float q = rintf(h2f(h) / s);   // IEEE fp32 division, ties to even
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (int)q;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+// Block-wide max of a uint32 (all threads get the result).
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *red)
+{
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (lane == 0)
+        red[wid] = v;
+    __syncthreads();
+    uint32_t r = red[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; i++)
+        r = max(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+// Max magnitude of the 8 binary16 values in v whose bit in `skip` is clear.
+__device__ __forceinline__ uint32_t masked_max8(uint4 v, uint32_t skip)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+        if (!((skip >> (2 * i)) & 1u))
+            m = max(m, lo);
+        if (!((skip >> (2 * i + 1)) & 1u))
+            m = max(m, hi);
+    }
+    return m;
+}
+
+// Codes of 8 values packed little-endian into two words; positions whose
+// bit in `skip` is set get code 0.
+__device__ __forceinline__ uint2 codes8(uint4 v, uint32_t skip, float s)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        int q = ((skip >> e) & 1u) ? 0 : code_of(h, s);
+        out[e >> 2] |= ((uint32_t)q & 0xffu) << (8 * (e & 3));
+    }
+    return make_uint2(out[0], out[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Weight quantization: one block per output feature n.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_quantize_weight(
+    const uint16_t *__restrict__ W, int K, int8_t *__restrict__ Wq, float *__restrict__ sW)
+{
+    __shared__ uint32_t red[kThreads / 64];
+    const int64_t n = blockIdx.x;
+    const uint4 *w = reinterpret_cast<const uint4 *>(W + n * (int64_t)K);
+    const int nchunk = K / 8;
+    uint32_t m = 0;
+    for (int c = threadIdx.x; c < nchunk; c += kThreads)
+        m = max(m, masked_max8(w[c], 0u));
+    m = block_max(m, red);
+    const float s = h2f(m) / 127.0f;
+    if (threadIdx.x == 0)
+        sW[n] = s;
+    uint2 *q = reinterpret_cast<uint2 *>(Wq + n * (int64_t)K);
+    for (int c = threadIdx.x; c < nchunk; c += kThreads)
+        q[c] = codes8(w[c], 0u, s);
+}
+
+// ---------------------------------------------------------------------------
+// Clear the outlier bit set and the meta words (a kernel rather than a
+// memset so that the sequence stays capturable in a HIP graph).
+// ---------------------------------------------------------------------------
+__global__ void k_clear(uint32_t *__restrict__ bits, int nwords, int32_t *__restrict__ meta)
+{
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nwords)
+        bits[i] = 0u;
+    if (i < 64)
+        meta[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Outlier detection.  Block (x, y) covers 2048 columns (8 per thread) of
+// rows [y*R, y*R+R).  The per-column magnitude max over those rows is
+// kept packed in registers; one compare per column at the end; four lanes
+// combine their 8-bit masks into one 32-bit word, and non-zero words are
+// OR-ed into the bit set.
+// ---------------------------------------------------------------------------
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+__global__ __launch_bounds__(kThreads) void k_detect(
+    const uint16_t *__restrict__ X, int T, int K, int R, uint32_t thr_mag,
+    uint32_t *__restrict__ bits)
+{
+    const int nchunk = K / 8;
+    const int c = blockIdx.x * kThreads + threadIdx.x;
+    const int t0 = blockIdx.y * R;
+    const int t1 = min(T, t0 + R);
+    us2 mx[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+    if (c < nchunk) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(X + (int64_t)t0 * K) + c;
+        const int64_t stride = K / 8;
+        int t = t0;
+        for (; t + 4 <= t1; t += 4) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                v[u] = p[u * stride];
+            p += 4 * stride;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    mx[i] = __builtin_elementwise_max(
+                        mx[i], __builtin_bit_cast(us2, w[i] & 0x7fff7fffu));
+            }
+        }
+        for (; t < t1; t++) {
+            uint4 v = *p;
+            p += stride;
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                mx[i] = __builtin_elementwise_max(mx[i], __builtin_bit_cast(us2, w[i] & 0x7fff7fffu));
+        }
+    }
+    uint32_t m8 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        m8 |= ((uint32_t)mx[i].x > thr_mag ? 1u : 0u) << (2 * i);
+        m8 |= ((uint32_t)mx[i].y > thr_mag ? 1u : 0u) << (2 * i + 1);
+    }
+    // chunk c holds columns 8c..8c+7 = bits 8*(c%4).. of word c/4
+    uint32_t word = m8 << (8 * (c & 3));
+    word |= (uint32_t)__shfl_xor((int)word, 1, 64);
+    word |= (uint32_t)__shfl_xor((int)word, 2, 64);
+    if ((c & 3) == 0 && c < nchunk && word != 0u)
+        atomicOr(bits + (c >> 2), word);
+}
+
+// Load the bit set into LDS and write the exclusive prefix of the
+// popcounts per word; returns nO (the total) to every thread.
+__device__ int load_bits_and_scan(const uint32_t *__restrict__ bits_g, int nw,
+                                  uint32_t *bits, int32_t *pre, int32_t *scan)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int per = (nw + kThreads - 1) / kThreads;
+    const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+    int s = 0;
+    for (int w = w0; w < w1; w++) {
+        uint32_t b = bits_g[w];
+        bits[w] = b;
+        s += __popc(b);
+    }
+    // inclusive scan within the wave
+    int v = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int u = __shfl_up(v, o, 64);
+        if (lane >= o)
+            v += u;
+    }
+    if (lane == 63)
+        scan[wid] = v;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; i++) {
+        if (i < wid)
+            base += scan[i];
+        total += scan[i];
+    }
+    int p = base + v - s;   // exclusive prefix of this thread's first word
+    for (int w = w0; w < w1; w++) {
+        pre[w] = p;
+        p += __popc(bits[w]);
+    }
+    __syncthreads();
+    return total;
+}
+
+// ---------------------------------------------------------------------------
+// Token quantization + outlier gathers.  Blocks [0, T) each quantize one
+// token row; blocks [T, T + ceil(N/wrows)) gather the outlier columns of
+// wrows rows of Wq.  Every block first rebuilds the prefix counts of the
+// bit set in LDS, which gives each outlier column its compact index.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_prepare(
+    const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq, int T, int K, int N,
+    int wrows, const uint32_t *__restrict__ bits_g, int32_t *__restrict__ meta,
+    int32_t *__restrict__ idx_g, float *__restrict__ sX, int8_t *__restrict__ Xq,
+    uint16_t *__restrict__ XO, int8_t *__restrict__ WO)
+{
+    extern __shared__ uint32_t smem[];
+    __shared__ int32_t scan[kThreads / 64];
+    __shared__ uint32_t red[kThreads / 64];
+    const int nw = (K + 31) / 32;
+    uint32_t *bits = smem;
+    int32_t *pre = reinterpret_cast<int32_t *>(smem + nw);
+    const int nO = load_bits_and_scan(bits_g, nw, bits, pre, scan);
+    const int nO16 = (nO + 15) & ~15;   // <= K since K % 16 == 0
+    const int tid = threadIdx.x;
+
+    if ((int)blockIdx.x < T) {
+        // ---- one token row ----
+        const int64_t t = blockIdx.x;
+        const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
+        const int nchunk = K / 8;
+        constexpr int RREG = 4;   // chunks per thread kept in registers
+        uint4 v[RREG];
+        uint32_t m = 0;
+#pragma unroll
+        for (int s = 0; s < RREG; s++) {
+            const int c = tid + s * kThreads;
+            if (c < nchunk) {
+                v[s] = xr[c];
+                m = max(m, masked_max8(v[s], (bits[c >> 2] >> (8 * (c & 3))) & 0xffu));
+            }
+        }
+        for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads)
+            m = max(m, masked_max8(xr[c], (bits[c >> 2] >> (8 * (c & 3))) & 0xffu));
+        m = block_max(m, red);
+        const float s = h2f(m) / 127.0f;
+        if (tid == 0)
+            sX[t] = s;
+        uint2 *q = reinterpret_cast<uint2 *>(Xq + t * K);
+        uint16_t *xo = XO + t * K;
+        auto emit = [&](int c, uint4 x) {
+            const uint32_t wbits = bits[c >> 2];
+            const uint32_t skip = (wbits >> (8 * (c & 3))) & 0xffu;
+            q[c] = codes8(x, skip, s);
+            if (skip) {
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                const int b0 = 8 * (c & 3);
+                int i = pre[c >> 2] + __popc(wbits & ((1u << b0) - 1u));
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    if ((skip >> e) & 1u)
+                        xo[i++] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            }
+        };
+#pragma unroll
+        for (int s2 = 0; s2 < RREG; s2++) {
+            const int c = tid + s2 * kThreads;
+            if (c < nchunk)
+                emit(c, v[s2]);
+        }
+        for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads)
+            emit(c, xr[c]);
+        if (tid < nO16 - nO)
+            xo[nO + tid] = 0;
+        return;
+    }
+
+    // ---- outlier columns of wrows weight rows ----
+    const int wb = blockIdx.x - T;
+    const int n0 = wb * wrows;
+    const int n1 = min(N, n0 + wrows);
+    if (wb == 0) {
+        for (int w = tid; w < nw; w += kThreads) {
+            uint32_t b = bits[w];
+            int p = pre[w];
+            while (b) {
+                idx_g[p++] = 32 * w + __ffs(b) - 1;
+                b &= b - 1u;
+            }
+        }
+        if (tid == 0)
+            meta[0] = nO;
+    }
+    if (nO == 0) {
+        // only the zero pad (none when nO == 0)
+        return;
+    }
+    const int pairs = (n1 - n0) * nw;
+    for (int p = tid; p < pairs; p += kThreads) {
+        const int n = n0 + p / nw;
+        const int w = p - (p / nw) * nw;
+        uint32_t b = bits[w];
+        if (!b)
+            continue;
+        const int8_t *src = Wq + (int64_t)n * K + 32 * w;
+        uint4 lo = *reinterpret_cast<const uint4 *>(src);
+        uint4 hi = make_uint4(0, 0, 0, 0);
+        if (32 * w + 16 < K)
+            hi = *reinterpret_cast<const uint4 *>(src + 16);
+        const uint32_t by[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        int8_t *dst = WO + (int64_t)n * K;
+        int i = pre[w];
+        while (b) {
+            const int j = __ffs(b) - 1;
+            dst[i++] = (int8_t)((by[j >> 2] >> (8 * (j & 3))) & 0xffu);
+            b &= b - 1u;
+        }
+    }
+    for (int p = tid; p < (n1 - n0) * 16; p += kThreads) {
+        const int n = n0 + p / 16, e = p % 16;
+        if (nO + e < nO16)
+            WO[(int64_t)n * K + nO + e] = 0;
+    }
+}
+
+} // namespace
+
+hipError_t launch_quantize_weight(const uint16_t *W, int64_t N, int64_t K, int8_t *Wq,
+                                  float *sW, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_quantize_weight, dim3((unsigned)N), dim3(kThreads), 0, s, W,
+                       (int)K, Wq, sW);
+    return hipGetLastError();
+}
+
+hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, uint16_t thr_mag, int64_t T,
+                          int64_t K, int64_t N, char *ws, const WsLayout &L, hipStream_t s)
+{
+    uint32_t *bits = reinterpret_cast<uint32_t *>(ws + L.bits);
+    int32_t *meta = reinterpret_cast<int32_t *>(ws + L.meta);
+    const int nw = (int)((K + 31) / 32);
+    hipLaunchKernelGGL(k_clear, dim3((unsigned)((max(nw, 64) + 255) / 256)), dim3(256), 0, s,
+                       bits, nw, meta);
+    const int nchunk = (int)(K / 8);
+    if (nchunk > 0) {
+        const int gx = (nchunk + kThreads - 1) / kThreads;
+        // about 8 rows per block; more when T is huge (grid.y <= 65535)
+        int R = 8;
+        while ((T + R - 1) / R > 65535)
+            R *= 2;
+        const int gy = (int)((T + R - 1) / R);
+        hipLaunchKernelGGL(k_detect, dim3(gx, gy), dim3(kThreads), 0, s, X, (int)T, (int)K,
+                           R, (uint32_t)thr_mag, bits);
+    }
+    const int wrows = 8;
+    const int64_t wblocks = (N + wrows - 1) / wrows;
+    const size_t lds = 8 * (size_t)(nw > 0 ? nw : 1);
+    hipLaunchKernelGGL(k_prepare, dim3((unsigned)(T + wblocks)), dim3(kThreads), lds, s, X, Wq,
+                       (int)T, (int)K, (int)N, wrows, bits, meta,
+                       reinterpret_cast<int32_t *>(ws + L.idx),
+                       reinterpret_cast<float *>(ws + L.sX),
+                       reinterpret_cast<int8_t *>(ws + L.Xq),
+                       reinterpret_cast<uint16_t *>(ws + L.XO),
+                       reinterpret_cast<int8_t *>(ws + L.WO));
+    return hipGetLastError();
+}
+
+} // namespace li8

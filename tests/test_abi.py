@@ -1,0 +1,142 @@
+"""The C ABI library: it loads, exports every declared symbol, and rejects bad
+arguments on the host with the documented status before launching anything.
+
+These run without a GPU: every call here fails validation, and validation
+makes no HIP call.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import int8_matmul_amd as li8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llm_int8.h")
+
+OK, INVALID, SHAPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 4
+# fake, never-dereferenced device addresses
+P = 0x7F0000000000
+P2 = 0x7F0000100000
+MIS = 0x7F0000000008  # 8-byte aligned only
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z][a-z0-9_]*)\s*\(", src)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(li8.library_path()):
+        import int8_matmul_amd.build as b
+        b.build()
+    return li8.load_library()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted([
+        "li8_status_str", "int8_quantize_weight", "llm_int8_workspace_bytes",
+        "llm_int8_linear", "llm_int8_prepare", "llm_int8_gemm", "llm_int8_export_stages",
+    ])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and they are C symbols (no C++ mangling)
+    raw = ctypes.CDLL(li8.library_path())
+    for name in declared_functions():
+        ctypes.cast(getattr(raw, name), ctypes.c_void_p)
+
+
+def test_status_strings(lib):
+    for code, name in li8.STATUS.items():
+        assert lib.li8_status_str(code).decode() == name
+    assert lib.li8_status_str(99).decode() == "LI8_UNKNOWN_STATUS"
+
+
+def test_workspace_bytes(lib):
+    ws = lib.llm_int8_workspace_bytes
+    assert ws(16, 17, 16) == 0          # K % 16
+    assert ws(-1, 16, 16) == 0
+    assert ws(16, 133152, 16) == 0      # K above the int32 bound
+    assert ws(16, 133136, 16) > 0
+    a = ws(4096, 4096, 11008)
+    # covers Xq (T*K), the gathered outlier columns of X (2*T*K) and of Wq
+    # (N*K) in the worst case nO = K, plus small tables
+    assert a >= 4096 * 4096 * 3 + 11008 * 4096
+    assert a < 4096 * 4096 * 3 + 11008 * 4096 + (1 << 20)
+    assert ws(0, 16, 16) > 0 and ws(16, 0, 16) > 0
+    assert ws(8, 4096, 4096) <= ws(16, 4096, 4096) <= ws(16, 4096, 8192)
+    assert a % 256 == 0
+
+
+def test_quantize_weight_validation(lib):
+    f = lib.int8_quantize_weight
+    assert f(P, 4, 17, P, P, None) == SHAPE
+    assert f(P, -1, 16, P, P, None) == SHAPE
+    assert f(None, 4, 16, P, P, None) == INVALID
+    assert f(P, 4, 16, None, P, None) == INVALID
+    assert f(P, 4, 16, P, None, None) == INVALID
+    assert f(MIS, 4, 16, P, P, None) == ALIGN
+    assert f(P, 4, 16, P, MIS, None) == ALIGN
+    assert f(None, 0, 16, None, None, None) == OK   # empty: nothing to do
+
+
+def test_linear_validation(lib):
+    f = lib.llm_int8_linear
+    need = lib.llm_int8_workspace_bytes(32, 64, 48)
+    args = dict(X=P, Wq=P, sW=P, thr=6.0, T=32, K=64, N=48, Y=P2, ws=P, wsb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["X"], a["Wq"], a["sW"], a["thr"], a["T"], a["K"], a["N"], a["Y"],
+                 a["ws"], a["wsb"], None)
+
+    assert call(K=24) == SHAPE
+    assert call(T=-3) == SHAPE
+    assert call(K=133152) == SHAPE
+    assert call(thr=-1.0) == INVALID
+    assert call(thr=math.nan) == INVALID
+    assert call(X=None) == INVALID
+    assert call(Wq=None) == INVALID
+    assert call(sW=None) == INVALID
+    assert call(Y=None) == INVALID
+    assert call(X=MIS) == ALIGN
+    assert call(Y=MIS) == ALIGN
+    assert call(ws=MIS) == ALIGN
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    # empty calls are valid and enqueue nothing, whatever the pointers
+    assert call(T=0, X=None, Y=None, ws=None, wsb=0) == OK
+    assert call(N=0, Wq=None, sW=None, Y=None, ws=None, wsb=0) == OK
+    assert call(T=0, thr=math.inf) == OK
+    assert call(T=0, thr=-0.0) == OK
+
+
+def test_prepare_and_gemm_validation(lib):
+    need = lib.llm_int8_workspace_bytes(32, 64, 48)
+    p = lib.llm_int8_prepare
+    assert p(None, P, 6.0, 32, 64, 48, P, need, None) == INVALID
+    assert p(P, P, math.nan, 32, 64, 48, P, need, None) == INVALID
+    assert p(P, P, 6.0, 32, 64, 48, P, need - 256, None) == WORKSPACE
+    assert p(P, P, 6.0, 32, 72, 48, P, need, None) == SHAPE
+    g = lib.llm_int8_gemm
+    assert g(P, P, 32, 64, 48, None, None, P, need, None) == INVALID
+    assert g(P, P, 32, 64, 48, P2, MIS, P, need, None) == ALIGN
+    assert g(P, P, 32, 64, 48, P2, None, P, 16, None) == WORKSPACE
+    assert g(P, P, 0, 64, 48, None, None, None, 0, None) == OK
+    e = lib.llm_int8_export_stages
+    assert e(None, 0, 32, 64, 48, None, None, None, None, None, None, None) == WORKSPACE
+    assert e(P, need, 32, 65, 48, None, None, None, None, None, None, None) == SHAPE
+
+
+def test_python_binding_rejects_cpu_tensors(lib):
+    import torch
+    W = torch.zeros(4, 16, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        li8.quantize_weight(W)
