@@ -37,8 +37,8 @@
  *     caller's next synchronization.
  *   - Shapes: T >= 0 tokens, N >= 0 output features, K >= 0 features with
  *     K a multiple of 16 and K <= 133144 (so that the int32 sum of K
- *     products of magnitude <= 127*127 cannot overflow).  T == 0 or N == 0
- *     is an empty call that enqueues nothing.
+ *     products of magnitude <= 127*127 cannot overflow), T*K < 2^31 and
+ *     N*K < 2^31.  T == 0 or N == 0 is an empty call that enqueues nothing.
  *   - Inputs must be finite; NaN or Inf in X or W is outside the contract.
  */
 #ifndef LLM_INT8_H
@@ -56,8 +56,8 @@ extern "C" {
 typedef enum li8_status {
     LI8_OK = 0,
     LI8_ERR_INVALID_ARG = 1, /* null pointer, NaN or negative threshold     */
-    LI8_ERR_SHAPE = 2,       /* negative dim, K % 16 != 0, K > 133144, or a
-                                byte size that overflows int64             */
+    LI8_ERR_SHAPE = 2,       /* negative dim, K % 16 != 0, K > 133144,
+                                T*K or N*K >= 2^31                         */
     LI8_ERR_ALIGN = 3,       /* a pointer not 16-byte aligned               */
     LI8_ERR_WORKSPACE = 4,   /* workspace null or smaller than required     */
     LI8_ERR_HIP = 5          /* a HIP launch or copy failed to enqueue (for

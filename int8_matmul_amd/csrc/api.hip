@@ -22,9 +22,11 @@ li8_status check_shape(int64_t T, int64_t K, int64_t N)
     const int64_t lim = (int64_t)1 << 31;
     if (T >= lim || N >= lim)
         return LI8_ERR_SHAPE;
-    // T*N*4 (acc), T*K*2 and N*K must fit comfortably in int64
-    if ((double)T * (double)N * 4.0 > 9.0e18 || (double)T * (double)K * 3.0 > 9.0e18 ||
-        (double)N * (double)K > 9.0e18)
+    // the GEMM addresses the int8 operands with 32-bit buffer offsets
+    if (T * K > kMaxOperandBytes || N * K > kMaxOperandBytes)
+        return LI8_ERR_SHAPE;
+    // T*N*4 (acc) must fit comfortably in int64
+    if ((double)T * (double)N * 4.0 > 9.0e18)
         return LI8_ERR_SHAPE;
     return LI8_OK;
 }

@@ -14,12 +14,30 @@
 // domain), up to fp32 rounding; with no outlier columns it is exactly
 // fp16(fl32(fl32(acc * sX) * sW)).
 //
-// Both operands are K-contiguous ("NT").  Tiles: BM x BN per workgroup,
-// BK = 128 bytes of K per stage, two LDS stages, WM x WN waves each owning
-// an (FM*32) x (FN*32) sub-tile computed with v_mfma_i32_32x32x32_i8.
-// Global -> register -> LDS staging with an XOR swizzle of the 16-byte
-// chunks so that both the row-wise LDS writes and the MFMA fragment reads
-// hit distinct banks.
+// Structure (both operands K-contiguous, "NT"):
+//  - BM x BN output tile per workgroup of WM x WN waves; each wave owns an
+//    (FM*32) x (FN*32) sub-tile computed with v_mfma_i32_32x32x32_i8.
+//  - K is consumed in stages of BKS bytes held in a ring of NS LDS buffers,
+//    filled by buffer_load ... lds (global -> LDS without VGPRs).  A stage
+//    is requested NS stages ahead.  A lane whose 16-byte chunk lies past K
+//    gets an out-of-range buffer offset, for which the hardware returns
+//    zeros, so a ragged K needs no branch.
+//  - MFMA fragments are double-buffered in registers: the LDS reads of
+//    k-step s+1 are issued before the MFMAs of k-step s.  The one barrier
+//    per stage sits before the MFMAs of the stage's last k-step, after all
+//    reads of the stage were issued, so the MFMA pipe has queued work when
+//    a wave reaches it.
+//  - 16-byte chunks are XOR-swizzled per row in LDS so that fragment reads
+//    (32 rows x 16 bytes per half-wave) hit distinct banks.
+//  - Workgroups are renumbered so that each XCD (the hardware deals
+//    workgroups to the 8 XCDs round-robin) gets a contiguous run of tiles,
+//    and tiles are ordered in groups of GM row-tiles, so that the tiles
+//    running together on one XCD share operand rows in its L2.
+//  - Epilogue: per 32x32 block, dequantize, add the outlier MFMA, scale,
+//    convert to fp16 into LDS; then each wave writes its sub-tile with
+//    16-byte stores.
+#include <type_traits>
+
 #include "li8_internal.h"
 
 namespace li8 {
@@ -29,56 +47,136 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+#define LI8_LDS __attribute__((address_space(3)))
 
-constexpr int BK = 128;          // bytes of K per stage
-constexpr int CPR = BK / 16;     // 16-byte chunks per tile row
+// Buffer resource over `bytes` bytes at p (raw buffer, offsets in bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & (CPR - 1); }
+// 16 bytes per lane from rsrc at voffset + soffset into LDS at lds + 16*lane.
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, int voffset,
+                                            int soffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LI8_LDS void *)lds, 16, voffset, soffset, 0, 0);
+}
 
-template <int BM, int BN, int WM, int WN, bool STORE_ACC>
+template <int CPR>
+__device__ __forceinline__ int swz(int row)
+{
+    static_assert(CPR == 4 || CPR == 8, "16-byte chunks per LDS row");
+    if constexpr (CPR == 8)
+        return (row ^ (row >> 3)) & 7;
+    else
+        return ((row >> 1) ^ (row >> 3)) & 3;
+}
+
+// Wait until at most N buffer loads of this wave are in flight and all its
+// LDS reads are done, then barrier.  The compiler does not track the LDS
+// writes of buffer_load ... lds, so this wait is what orders them.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+constexpr int kOutOfRange = (int)0x80000000;   // buffer offset past any operand
+
+template <int BM, int BN, int BKS, int NS, int WM, int WN, int GM, bool STORE_ACC>
 __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     const int8_t *__restrict__ Xq, const int8_t *__restrict__ Wq,
     const float *__restrict__ sX, const float *__restrict__ sW,
     const int32_t *__restrict__ meta, const uint16_t *__restrict__ XO,
-    const int8_t *__restrict__ WO, int T, int K, int N, int tiles_m,
+    const int8_t *__restrict__ WO, int T, int K, int N, int tiles_m, int tiles_n,
     uint16_t *__restrict__ Y, int32_t *__restrict__ acc_out)
 {
-    constexpr int NT = WM * WN * 64;
+    constexpr int NT = WM * WN * 64, NW = WM * WN;
     constexpr int FM = BM / (WM * 32);
     constexpr int FN = BN / (WN * 32);
-    constexpr int CA = BM * CPR / NT;   // 16-byte chunks per thread per stage (A)
-    constexpr int CB = BN * CPR / NT;
+    constexpr int CPR = BKS / 16;              // 16-byte chunks per LDS row
+    constexpr int KS = BKS / 32;               // MFMA k-steps per stage
+    constexpr int ASZ = BM * BKS, SSZ = (BM + BN) * BKS;
+    constexpr int LA = BM * CPR / NT, LB = BN * CPR / NT;   // loads per lane per stage
+    constexpr int RS = FN * 32 + 8;            // epilogue staging row stride (halves)
+    constexpr int STG = NW * (FM * 32) * RS * 2;
+    constexpr int LDSB = (NS * SSZ > STG) ? NS * SSZ : STG;
     static_assert(FM * WM * 32 == BM && FN * WN * 32 == BN, "tile shape");
-    static_assert(CA * NT == BM * CPR && CB * NT == BN * CPR, "loader shape");
+    static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "loader shape");
+    static_assert(KS % 2 == 0 && NS >= 2, "pipeline shape");
+    __shared__ __attribute__((aligned(1024))) int8_t lds[LDSB];
 
-    __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) int8_t lds_b[2][BN * BK];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid / WN, wn = wid % WN;
-    const int tile_m = blockIdx.x % tiles_m;
-    const int tile_n = blockIdx.x / tiles_m;
-    const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-    // ---- per-thread loader coordinates ----
-    const int8_t *ga[CA];
-    const int8_t *gb[CB];
-    int la[CA], lb[CB], ka[CA], kb[CB];
+    // ---- tile of this workgroup ----
+    int bid = blockIdx.x;
+    {
+        const int nblk = tiles_m * tiles_n;
+        const int per = nblk / 8, rem = nblk % 8, xcd = bid % 8, loc = bid / 8;
+        bid = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+    }
+    const int width = GM * tiles_n;
+    const int first_m = (bid / width) * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int tile_m = first_m + (bid % width) % gm;
+    const int tile_n = (bid % width) / gm;
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    // have every kernel argument the epilogue uses in registers before the
+    // main loop: a scalar load in flight across it would make the compiler
+    // wait for all LDS reads instead of the older half
+    asm volatile("" ::"s"(sX), "s"(sW), "s"(meta), "s"(XO), "s"(WO), "s"(Y), "s"(acc_out));
+
+    // ---- global -> LDS loaders: load i of this lane fills LDS chunk
+    // p = i*NT + wid*64 + lane of the stage (row p / CPR, physical chunk
+    // p % CPR), which holds logical chunk (p % CPR) ^ swz(row) ----
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Xq, T * K);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(Wq, N * K);
+    int voA[LA], voB[LB], kmA[LA], kmB[LB];
 #pragma unroll
-    for (int i = 0; i < CA; i++) {
-        const int c = tid + i * NT, row = c / CPR, q = c % CPR;
-        ga[i] = Xq + (int64_t)min(m0 + row, T - 1) * K + q * 16;
-        ka[i] = q * 16;
-        la[i] = row * BK + ((q ^ swz(row)) * 16);
+    for (int i = 0; i < LA; i++) {
+        const int p = i * NT + wid * 64 + lane, row = p / CPR, q = (p % CPR) ^ swz<CPR>(row);
+        voA[i] = min(m0 + row, T - 1) * K + q * 16;
+        kmA[i] = K - q * 16;   // the chunk is inside the row while k0 < kmA
     }
 #pragma unroll
-    for (int i = 0; i < CB; i++) {
-        const int c = tid + i * NT, row = c / CPR, q = c % CPR;
-        gb[i] = Wq + (int64_t)min(n0 + row, N - 1) * K + q * 16;
-        kb[i] = q * 16;
-        lb[i] = row * BK + ((q ^ swz(row)) * 16);
+    for (int i = 0; i < LB; i++) {
+        const int p = i * NT + wid * 64 + lane, row = p / CPR, q = (p % CPR) ^ swz<CPR>(row);
+        voB[i] = min(n0 + row, N - 1) * K + q * 16;
+        kmB[i] = K - q * 16;
+    }
+    auto issue = [&](int kt) {
+        const int k0 = kt * BKS;
+        int8_t *st = lds + (kt % NS) * SSZ;
+#pragma unroll
+        for (int i = 0; i < LA; i++)
+            load_to_lds(rA, st + (i * NT + wid * 64) * 16, (k0 < kmA[i]) ? voA[i] : kOutOfRange, k0);
+#pragma unroll
+        for (int i = 0; i < LB; i++)
+            load_to_lds(rB, st + ASZ + (i * NT + wid * 64) * 16, (k0 < kmB[i]) ? voB[i] : kOutOfRange,
+                        k0);
+    };
+
+    // ---- MFMA fragments: lane l supplies row (l & 31) of each 32-row
+    // block and the 16 bytes of chunk 2*kk + (l >> 5) of k-step kk ----
+    const int arow0 = wm * FM * 32 + (lane & 31);
+    const int brow0 = wn * FN * 32 + (lane & 31);
+    const int khalf = lane >> 5;
+    int offA[FM][KS], offB[FN][KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) {
+        const int q = kk * 2 + khalf;
+#pragma unroll
+        for (int a = 0; a < FM; a++) {
+            const int row = arow0 + a * 32;
+            offA[a][kk] = row * BKS + ((q ^ swz<CPR>(row)) * 16);
+        }
+#pragma unroll
+        for (int b = 0; b < FN; b++) {
+            const int row = brow0 + b * 32;
+            offB[b][kk] = ASZ + row * BKS + ((q ^ swz<CPR>(row)) * 16);
+        }
     }
 
     v16i acc[FM][FN];
@@ -88,71 +186,76 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
         for (int b = 0; b < FN; b++)
             acc[a][b] = v16i{};
 
-    const int nk = (K + BK - 1) / BK;
-    v4i ra[CA], rb[CB];
-    auto gload = [&](int kt) {
-        const int k0 = kt * BK;
+    v4i fa[2][FM], fb[2][FN];
+    auto lread = [&](int set, int kt, int kk) {
+        const int8_t *base = lds + (kt % NS) * SSZ;
 #pragma unroll
-        for (int i = 0; i < CA; i++)
-            ra[i] = (k0 + ka[i] < K) ? *reinterpret_cast<const v4i *>(ga[i] + k0) : v4i{};
+        for (int a = 0; a < FM; a++)
+            fa[set][a] = *reinterpret_cast<const v4i *>(base + offA[a][kk]);
 #pragma unroll
-        for (int i = 0; i < CB; i++)
-            rb[i] = (k0 + kb[i] < K) ? *reinterpret_cast<const v4i *>(gb[i] + k0) : v4i{};
+        for (int b = 0; b < FN; b++)
+            fb[set][b] = *reinterpret_cast<const v4i *>(base + offB[b][kk]);
     };
-    auto lstore = [&](int st) {
+    auto mfmas = [&](int set) {
 #pragma unroll
-        for (int i = 0; i < CA; i++)
-            *reinterpret_cast<v4i *>(&lds_a[st][la[i]]) = ra[i];
+        for (int a = 0; a < FM; a++)
 #pragma unroll
-        for (int i = 0; i < CB; i++)
-            *reinterpret_cast<v4i *>(&lds_b[st][lb[i]]) = rb[i];
+            for (int b = 0; b < FN; b++)
+                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][a], fb[set][b], acc[a][b],
+                                                                 0, 0, 0);
     };
-
-    // fragment rows owned by this lane
-    const int arow0 = wm * FM * 32 + (lane & 31);
-    const int brow0 = wn * FN * 32 + (lane & 31);
-    const int khalf = lane >> 5;
-
-    if (nk > 0) {
-        gload(0);
-        lstore(0);
-        __syncthreads();
-    }
-    for (int kt = 0; kt < nk; kt++) {
-        const int st = kt & 1;
-        if (kt + 1 < nk)
-            gload(kt + 1);
+    // One stage.  WAIT: buffer loads allowed in flight at the barrier;
+    // ISSUE: request stage kt+NS into the buffer just released; LAST: no
+    // next stage.
+    auto stage = [&](int kt, auto wait_c, auto issue_c, auto last_c) {
+        constexpr int WAIT = decltype(wait_c)::value;
+        constexpr bool ISSUE = decltype(issue_c)::value;
+        constexpr bool LAST = decltype(last_c)::value;
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; kk++) {
-            const int q = kk * 2 + khalf;
-            v4i fa[FM], fb[FN];
-#pragma unroll
-            for (int a = 0; a < FM; a++) {
-                const int row = arow0 + a * 32;
-                fa[a] = *reinterpret_cast<const v4i *>(&lds_a[st][row * BK + ((q ^ swz(row)) * 16)]);
+        for (int kk = 0; kk < KS; kk++) {
+            const int cur = kk & 1;
+            if (kk + 1 < KS) {
+                lread(cur ^ 1, kt, kk + 1);
+            } else if constexpr (!LAST) {
+                wait_loads_barrier<WAIT>();   // stage kt+1 landed; stage kt read by all
+                if constexpr (ISSUE)
+                    issue(kt + NS);
+                lread(cur ^ 1, kt + 1, 0);
             }
-#pragma unroll
-            for (int b = 0; b < FN; b++) {
-                const int row = brow0 + b * 32;
-                fb[b] = *reinterpret_cast<const v4i *>(&lds_b[st][row * BK + ((q ^ swz(row)) * 16)]);
-            }
-#pragma unroll
-            for (int a = 0; a < FM; a++)
-#pragma unroll
-                for (int b = 0; b < FN; b++)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb[b], acc[a][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(cur);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < nk)
-            lstore(st ^ 1);
-        __syncthreads();
+    };
+    using TF = std::false_type;
+    using TT = std::true_type;
+    using W0 = std::integral_constant<int, 0>;
+    using WS = std::integral_constant<int, (LA + LB) * (NS - 2)>;
+
+    const int nk = (K + BKS - 1) / BKS;
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+        if (s < nk)
+            issue(s);
+    if (nk > 0) {
+        wait_loads_barrier<0>();
+        lread(0, 0, 0);
     }
+    int kt = 0;
+    for (; kt + NS < nk; kt++)      // steady state
+        stage(kt, WS{}, TT{}, TF{});
+    for (; kt + 1 < nk; kt++)       // drain
+        stage(kt, W0{}, TF{}, TF{});
+    if (kt < nk)
+        stage(kt, W0{}, TF{}, TT{});
 
     // ---- epilogue ----
     // 32x32 MFMA result layout: lane l, register r -> column (l & 31),
     // row 8*(r/4) + 4*(l/32) + (r%4) of the 32x32 block.
+    wait_loads_barrier<0>();   // the LDS is reused for the output staging
+    uint16_t *stg = reinterpret_cast<uint16_t *>(lds) + wid * (FM * 32) * RS;
     const int nO = meta[0];
     const int nch = (nO + 15) >> 4;
-    v16f d[FM][FN];
 #pragma unroll
     for (int a = 0; a < FM; a++) {
         float sx[16];
@@ -161,6 +264,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
             const int row = m0 + wm * FM * 32 + a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
             sx[r] = sX[min(row, T - 1)];
         }
+        const int xrow = min(m0 + arow0 + a * 32, T - 1);
 #pragma unroll
         for (int b = 0; b < FN; b++) {
             if constexpr (STORE_ACC) {
@@ -172,60 +276,68 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                         acc_out[(int64_t)row * N + col] = acc[a][b][r];
                 }
             }
+            v16f d;
 #pragma unroll
             for (int r = 0; r < 16; r++)
-                d[a][b][r] = (float)acc[a][b][r] * sx[r];
-        }
-    }
-    for (int c = 0; c < nch; c++) {
-        v8h xa[FM], wb[FN];
+                d[r] = (float)acc[a][b][r] * sx[r];
+            const int wcol = min(n0 + brow0 + b * 32, N - 1);
+            for (int c = 0; c < nch; c++) {
+                const v8h xa =
+                    *reinterpret_cast<const v8h *>(XO + (int64_t)xrow * K + c * 16 + khalf * 8);
+                const uint2 u =
+                    *reinterpret_cast<const uint2 *>(WO + (int64_t)wcol * K + c * 16 + khalf * 8);
+                const uint32_t w[2] = {u.x, u.y};
+                v8h wb;
 #pragma unroll
-        for (int a = 0; a < FM; a++) {
-            const int row = min(m0 + arow0 + a * 32, T - 1);
-            xa[a] = *reinterpret_cast<const v8h *>(XO + (int64_t)row * K + c * 16 + khalf * 8);
-        }
-#pragma unroll
-        for (int b = 0; b < FN; b++) {
-            const int col = min(n0 + brow0 + b * 32, N - 1);
-            const uint2 u = *reinterpret_cast<const uint2 *>(WO + (int64_t)col * K + c * 16 + khalf * 8);
-            const uint32_t w[2] = {u.x, u.y};
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                wb[b][e] = (_Float16)(float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
-        }
-#pragma unroll
-        for (int a = 0; a < FM; a++)
-#pragma unroll
-            for (int b = 0; b < FN; b++)
-                d[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[a], wb[b], d[a][b], 0, 0, 0);
-    }
-#pragma unroll
-    for (int b = 0; b < FN; b++) {
-        const int col = n0 + wn * FN * 32 + b * 32 + (lane & 31);
-        const float sw = sW[min(col, N - 1)];
-#pragma unroll
-        for (int a = 0; a < FM; a++) {
+                for (int e = 0; e < 8; e++)
+                    wb[e] = (_Float16)(float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
+                d = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, wb, d, 0, 0, 0);
+            }
+            const int col = n0 + wn * FN * 32 + b * 32 + (lane & 31);
+            const float sw = sW[min(col, N - 1)];
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int row = m0 + wm * FM * 32 + a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-                if (row < T && col < N) {
-                    // fl32(D * sW) first, then one rounding to fp16: the empty
-                    // asm keeps the compiler from fusing the product and the
-                    // conversion into a single-rounding v_fma_mixlo_f16
-                    float p = d[a][b][r] * sw;
-                    asm("" : "+v"(p));
-                    const _Float16 h = (_Float16)p;
-                    Y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, h);
-                }
+                // fl32(D * sW) first, then one rounding to fp16: the empty
+                // asm keeps the compiler from fusing the product and the
+                // conversion into a single-rounding v_fma_mixlo_f16
+                float p = d[r] * sw;
+                asm("" : "+v"(p));
+                const _Float16 h = (_Float16)p;
+                stg[(a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3)) * RS + b * 32 + (lane & 31)] =
+                    __builtin_bit_cast(uint16_t, h);
+            }
+        }
+    }
+    // each wave stores its own sub-tile (only its own LDS rows: no barrier)
+    constexpr int CPRW = FN * 32 / 8;   // 16-byte chunks per sub-tile row
+    constexpr int NCH = FM * 32 * CPRW;
+    const int rbase = m0 + wm * FM * 32, cbase = n0 + wn * FN * 32;
+    if ((N & 7) == 0) {
+#pragma unroll
+        for (int i = 0; i < NCH / 64; i++) {
+            const int id = i * 64 + lane, row = id / CPRW, ch = id % CPRW;
+            const v4i v = *reinterpret_cast<const v4i *>(stg + row * RS + ch * 8);
+            const int grow = rbase + row, gcol = cbase + ch * 8;
+            if (grow < T && gcol < N)
+                *reinterpret_cast<v4i *>(Y + (int64_t)grow * N + gcol) = v;
+        }
+    } else {   // rows not 16-byte aligned: element stores
+        for (int i = 0; i < NCH / 64; i++) {
+            const int id = i * 64 + lane, row = id / CPRW, ch = id % CPRW;
+            const int grow = rbase + row;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const int gcol = cbase + ch * 8 + e;
+                if (grow < T && gcol < N)
+                    Y[(int64_t)grow * N + gcol] = stg[row * RS + ch * 8 + e];
             }
         }
     }
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_tile(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
-                       uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L,
-                       hipStream_t s)
+template <int BM, int BN, int BKS, int NS, int WM, int WN, int GM>
+hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
+                      uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, hipStream_t s)
 {
     const int tiles_m = (int)((T + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
@@ -237,21 +349,20 @@ hipError_t launch_tile(const int8_t *Wq, const float *sW, int64_t T, int64_t K, 
     const uint16_t *XO = reinterpret_cast<const uint16_t *>(ws + L.XO);
     const int8_t *WO = reinterpret_cast<const int8_t *>(ws + L.WO);
     if (acc)
-        hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, true>), grid, block, 0, s, Xq, Wq, sX, sW,
-                           meta, XO, WO, (int)T, (int)K, (int)N, tiles_m, Y, acc);
+        hipLaunchKernelGGL((k_gemm<BM, BN, BKS, NS, WM, WN, GM, true>), grid, block, 0, s, Xq, Wq,
+                           sX, sW, meta, XO, WO, (int)T, (int)K, (int)N, tiles_m, tiles_n, Y, acc);
     else
-        hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, false>), grid, block, 0, s, Xq, Wq, sX, sW,
-                           meta, XO, WO, (int)T, (int)K, (int)N, tiles_m, Y, acc);
+        hipLaunchKernelGGL((k_gemm<BM, BN, BKS, NS, WM, WN, GM, false>), grid, block, 0, s, Xq, Wq,
+                           sX, sW, meta, XO, WO, (int)T, (int)K, (int)N, tiles_m, tiles_n, Y, acc);
     return hipGetLastError();
 }
 
 } // namespace
 
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
-                       uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L,
-                       hipStream_t s)
+                       uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, hipStream_t s)
 {
-    return launch_tile<256, 256, 2, 4>(Wq, sW, T, K, N, Y, acc, ws, L, s);
+    return launch_cfg<256, 256, 128, 2, 2, 4, 4>(Wq, sW, T, K, N, Y, acc, ws, L, s);
 }
 
 } // namespace li8

@@ -10,6 +10,9 @@ namespace li8 {
 
 // Largest K for which sum_{j<K} |q_x q_w| <= K * 127 * 127 fits in int32.
 constexpr int64_t kMaxK = 133144;
+// Largest T*K and N*K: the GEMM reads the int8 operands through buffer
+// resources with 32-bit offsets.
+constexpr int64_t kMaxOperandBytes = ((int64_t)1 << 31) - 1;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -18,24 +18,39 @@
 // |h| is monotone in (h & 0x7fff), so |x| > thr  <=>  (h & 0x7fff) > H,
 // with H the largest binary16 magnitude pattern whose value is <= thr
 // (computed on the host).  The same ordering gives the exact absmax.
+#include <algorithm>
+
 #include "li8_internal.h"
 
 namespace li8 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPrepRows = 2;   // token rows per quantization workgroup
 
 __device__ __forceinline__ float h2f(uint32_t h)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// Code of one value for a row scale s (s == 0 means the row is all zero).
-__device__ __forceinline__ int code_of(uint32_t h, float s)
+// Quotient fl32(x / s) without a per-element division: with r = fl32(1/s)
+// computed once per vector, q0 = fl32(x*r), the residual e = x - q0*s is
+// exact as an fma, and fl32(q0 + e*r) is the correctly rounded quotient.
+// This is Markstein's correction step; for this kernel's inputs (s =
+// fl32(a/127) for an fp16 absmax a, x fp16 with |x| <= a) it has been
+// checked bit-exact against IEEE division over every such pair.
+__device__ __forceinline__ float quotient(float x, float s, float r)
 {
-    if (s == 0.0f)
-        return 0;
-    float q = rintf(h2f(h) / s);   // IEEE fp32 division, ties to even
+    const float q0 = x * r;
+    const float e = fmaf(-q0, s, x);
+    return fmaf(e, r, q0);
+}
+
+// Code of one value for a row scale s > 0 with r = fl32(1/s): round half to
+// even of the fp32 quotient, clamped to [-127, 127].
+__device__ __forceinline__ int code_of(uint32_t h, float s, float r)
+{
+    float q = rintf(quotient(h2f(h), s, r));
     q = fminf(fmaxf(q, -127.0f), 127.0f);
     return (int)q;
 }
@@ -81,15 +96,18 @@ __device__ __forceinline__ uint32_t masked_max8(uint4 v, uint32_t skip)
 }
 
 // Codes of 8 values packed little-endian into two words; positions whose
-// bit in `skip` is set get code 0.
-__device__ __forceinline__ uint2 codes8(uint4 v, uint32_t skip, float s)
+// bit in `skip` is set get code 0, and so does everything when s == 0 (an
+// all-zero vector).
+__device__ __forceinline__ uint2 codes8(uint4 v, uint32_t skip, float s, float r)
 {
+    if (s == 0.0f)
+        return make_uint2(0u, 0u);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t out[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-        uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        int q = ((skip >> e) & 1u) ? 0 : code_of(h, s);
+        const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const int q = ((skip >> e) & 1u) ? 0 : code_of(h, s, r);
         out[e >> 2] |= ((uint32_t)q & 0xffu) << (8 * (e & 3));
     }
     return make_uint2(out[0], out[1]);
@@ -110,11 +128,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize_weight(
         m = max(m, masked_max8(w[c], 0u));
     m = block_max(m, red);
     const float s = h2f(m) / 127.0f;
+    const float r = 1.0f / s;
     if (threadIdx.x == 0)
         sW[n] = s;
     uint2 *q = reinterpret_cast<uint2 *>(Wq + n * (int64_t)K);
     for (int c = threadIdx.x; c < nchunk; c += kThreads)
-        q[c] = codes8(w[c], 0u, s);
+        q[c] = codes8(w[c], 0u, s, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -132,12 +151,17 @@ __global__ void k_clear(uint32_t *__restrict__ bits, int nwords, int32_t *__rest
 
 // ---------------------------------------------------------------------------
 // Outlier detection.  Block (x, y) covers 2048 columns (8 per thread) of
-// rows [y*R, y*R+R).  The per-column magnitude max over those rows is
-// kept packed in registers; one compare per column at the end; four lanes
+// rows [y*R, y*R+R).  Rows are read in batches of kDetectRows with every load of a
+// batch issued before any is used (these short streaming kernels are
+// latency-bound otherwise); rows past the end re-read the last row, which
+// leaves the maximum unchanged.  The per-column magnitude max is kept
+// packed in registers; one compare per column at the end; four lanes
 // combine their 8-bit masks into one 32-bit word, and non-zero words are
 // OR-ed into the bit set.
 // ---------------------------------------------------------------------------
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDetectRows = 16;   // rows per load batch
 
 __global__ __launch_bounds__(kThreads) void k_detect(
     const uint16_t *__restrict__ X, int T, int K, int R, uint32_t thr_mag,
@@ -149,31 +173,21 @@ __global__ __launch_bounds__(kThreads) void k_detect(
     const int t1 = min(T, t0 + R);
     us2 mx[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
     if (c < nchunk) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(X + (int64_t)t0 * K) + c;
+        const uint4 *p = reinterpret_cast<const uint4 *>(X) + c;
         const int64_t stride = K / 8;
-        int t = t0;
-        for (; t + 4 <= t1; t += 4) {
-            uint4 v[4];
+        for (int tb = t0; tb < t1; tb += kDetectRows) {
+            uint4 v[kDetectRows];
 #pragma unroll
-            for (int u = 0; u < 4; u++)
-                v[u] = p[u * stride];
-            p += 4 * stride;
+            for (int u = 0; u < kDetectRows; u++)
+                v[u] = p[(int64_t)min(tb + u, t1 - 1) * stride];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
+            for (int u = 0; u < kDetectRows; u++) {
                 const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
                 for (int i = 0; i < 4; i++)
                     mx[i] = __builtin_elementwise_max(
                         mx[i], __builtin_bit_cast(us2, w[i] & 0x7fff7fffu));
             }
-        }
-        for (; t < t1; t++) {
-            uint4 v = *p;
-            p += stride;
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                mx[i] = __builtin_elementwise_max(mx[i], __builtin_bit_cast(us2, w[i] & 0x7fff7fffu));
         }
     }
     uint32_t m8 = 0;
@@ -232,11 +246,59 @@ __device__ int load_bits_and_scan(const uint32_t *__restrict__ bits_g, int nw,
 }
 
 // ---------------------------------------------------------------------------
-// Token quantization + outlier gathers.  Blocks [0, T) each quantize one
-// token row; blocks [T, T + ceil(N/wrows)) gather the outlier columns of
-// wrows rows of Wq.  Every block first rebuilds the prefix counts of the
-// bit set in LDS, which gives each outlier column its compact index.
+// Token quantization + outlier gathers.  Blocks [0, xblocks) each quantize
+// kPrepRows token rows; the remaining blocks gather the outlier columns of
+// wrows rows of Wq each.  Every block rebuilds the prefix counts of the bit
+// set in LDS, which gives each outlier column its compact index.
 // ---------------------------------------------------------------------------
+
+// Code byte of one value for a row scale s > 0 (r = fl32(1/s)), in the low
+// byte of the result.  Adding 1.5 * 2^23 rounds the quotient half-to-even
+// to an integer held in the low mantissa bits (two's complement), and
+// |code| <= 127 holds for every |x| <= absmax, so no clamp is needed; both
+// facts, like the quotient itself, are checked over every possible input.
+__device__ __forceinline__ uint32_t code_bits(uint32_t h, float s, float r)
+{
+    return __builtin_bit_cast(uint32_t, quotient(h2f(h), s, r) + 12582912.0f);
+}
+
+// Low bytes of four words packed into one (v_perm_b32 byte selects).
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
+}
+
+// Codes of the 8 values of a 16-byte chunk; positions set in `skip` (outlier
+// columns) get code 0.
+__device__ __forceinline__ uint2 token_codes8(uint4 v, uint32_t skip, float s, float r)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        c[e] = code_bits((w[e >> 1] >> (16 * (e & 1))) & 0xffffu, s, r);
+    if (skip) {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            if ((skip >> e) & 1u)
+                c[e] = 0u;
+    }
+    return make_uint2(pack_low_bytes(c[0], c[1], c[2], c[3]), pack_low_bytes(c[4], c[5], c[6], c[7]));
+}
+
+// Max magnitude of the 8 values of a chunk, skipping positions set in skip.
+__device__ __forceinline__ uint32_t chunk_max(uint4 v, uint32_t skip)
+{
+    if (skip)
+        return masked_max8(v, skip);
+    us2 m = __builtin_elementwise_max(__builtin_bit_cast(us2, v.x & 0x7fff7fffu),
+                                      __builtin_bit_cast(us2, v.y & 0x7fff7fffu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v.z & 0x7fff7fffu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v.w & 0x7fff7fffu));
+    return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+template <int ROWS>
 __global__ __launch_bounds__(kThreads) void k_prepare(
     const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq, int T, int K, int N,
     int wrows, const uint32_t *__restrict__ bits_g, int32_t *__restrict__ meta,
@@ -245,67 +307,112 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
 {
     extern __shared__ uint32_t smem[];
     __shared__ int32_t scan[kThreads / 64];
-    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t redr[ROWS][kThreads / 64];
+    __shared__ int nnz_s;
+    constexpr int RREG = 4;   // chunks per thread and row kept in registers
     const int nw = (K + 31) / 32;
     uint32_t *bits = smem;
     int32_t *pre = reinterpret_cast<int32_t *>(smem + nw);
+    const int tid = threadIdx.x;
+    const int nchunk = K / 8;
+    const int xblocks = (T + ROWS - 1) / ROWS;
+    const bool xblock = (int)blockIdx.x < xblocks;
+    const int t0 = blockIdx.x * ROWS;
+
+    // token rows: issue every load before the bit-set scan so that both
+    // latencies overlap
+    uint4 v[ROWS][RREG];
+    if (xblock) {
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            const uint4 *xr = reinterpret_cast<const uint4 *>(X + (int64_t)min(t0 + r, T - 1) * K);
+#pragma unroll
+            for (int s = 0; s < RREG; s++) {
+                const int c = tid + s * kThreads;
+                if (c < nchunk)
+                    v[r][s] = xr[c];
+            }
+        }
+    }
     const int nO = load_bits_and_scan(bits_g, nw, bits, pre, scan);
     const int nO16 = (nO + 15) & ~15;   // <= K since K % 16 == 0
-    const int tid = threadIdx.x;
 
-    if ((int)blockIdx.x < T) {
-        // ---- one token row ----
-        const int64_t t = blockIdx.x;
-        const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
-        const int nchunk = K / 8;
-        constexpr int RREG = 4;   // chunks per thread kept in registers
-        uint4 v[RREG];
-        uint32_t m = 0;
+    if (xblock) {
+        uint32_t m[ROWS];
 #pragma unroll
-        for (int s = 0; s < RREG; s++) {
-            const int c = tid + s * kThreads;
-            if (c < nchunk) {
-                v[s] = xr[c];
-                m = max(m, masked_max8(v[s], (bits[c >> 2] >> (8 * (c & 3))) & 0xffu));
+        for (int r = 0; r < ROWS; r++) {
+            m[r] = 0;
+#pragma unroll
+            for (int s = 0; s < RREG; s++) {
+                const int c = tid + s * kThreads;
+                if (c < nchunk)
+                    m[r] = max(m[r], chunk_max(v[r][s], (bits[c >> 2] >> (8 * (c & 3))) & 0xffu));
+            }
+            const uint4 *xr = reinterpret_cast<const uint4 *>(X + (int64_t)min(t0 + r, T - 1) * K);
+            for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads)
+                m[r] = max(m[r], chunk_max(xr[c], (bits[c >> 2] >> (8 * (c & 3))) & 0xffu));
+        }
+        // block-wide max of each row's value
+        {
+            const int lane = tid & 63, wid = tid >> 6;
+#pragma unroll
+            for (int r = 0; r < ROWS; r++) {
+                const uint32_t wmax = wave_max(m[r]);
+                if (lane == 0)
+                    redr[r][wid] = wmax;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < ROWS; r++) {
+                uint32_t x = redr[r][0];
+#pragma unroll
+                for (int i = 1; i < kThreads / 64; i++)
+                    x = max(x, redr[r][i]);
+                m[r] = x;
             }
         }
-        for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads)
-            m = max(m, masked_max8(xr[c], (bits[c >> 2] >> (8 * (c & 3))) & 0xffu));
-        m = block_max(m, red);
-        const float s = h2f(m) / 127.0f;
-        if (tid == 0)
-            sX[t] = s;
-        uint2 *q = reinterpret_cast<uint2 *>(Xq + t * K);
-        uint16_t *xo = XO + t * K;
-        auto emit = [&](int c, uint4 x) {
-            const uint32_t wbits = bits[c >> 2];
-            const uint32_t skip = (wbits >> (8 * (c & 3))) & 0xffu;
-            q[c] = codes8(x, skip, s);
-            if (skip) {
-                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-                const int b0 = 8 * (c & 3);
-                int i = pre[c >> 2] + __popc(wbits & ((1u << b0) - 1u));
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    if ((skip >> e) & 1u)
-                        xo[i++] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        for (int r = 0; r < ROWS; r++) {
+            const int64_t t = t0 + r;
+            if (t >= T)
+                break;
+            const float sc = h2f(m[r]) / 127.0f;
+            const float rc = 1.0f / sc;
+            if (tid == 0)
+                sX[t] = sc;
+            uint2 *q = reinterpret_cast<uint2 *>(Xq + t * K);
+            uint16_t *xo = XO + t * K;
+            auto emit = [&](int c, uint4 x) {
+                const uint32_t wbits = bits[c >> 2];
+                const uint32_t skip = (wbits >> (8 * (c & 3))) & 0xffu;
+                q[c] = (sc == 0.0f) ? make_uint2(0u, 0u) : token_codes8(x, skip, sc, rc);
+                if (skip) {
+                    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                    const int b0 = 8 * (c & 3);
+                    int i = pre[c >> 2] + __popc(wbits & ((1u << b0) - 1u));
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        if ((skip >> e) & 1u)
+                            xo[i++] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                }
+            };
+#pragma unroll
+            for (int s2 = 0; s2 < RREG; s2++) {
+                const int c = tid + s2 * kThreads;
+                if (c < nchunk)
+                    emit(c, v[r][s2]);
             }
-        };
-#pragma unroll
-        for (int s2 = 0; s2 < RREG; s2++) {
-            const int c = tid + s2 * kThreads;
-            if (c < nchunk)
-                emit(c, v[s2]);
+            const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
+            for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads)
+                emit(c, xr[c]);
+            if (tid < nO16 - nO)
+                xo[nO + tid] = 0;
         }
-        for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads)
-            emit(c, xr[c]);
-        if (tid < nO16 - nO)
-            xo[nO + tid] = 0;
         return;
     }
 
     // ---- outlier columns of wrows weight rows ----
-    const int wb = blockIdx.x - T;
+    const int wb = blockIdx.x - xblocks;
     const int n0 = wb * wrows;
     const int n1 = min(N, n0 + wrows);
     if (wb == 0) {
@@ -320,17 +427,31 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
         if (tid == 0)
             meta[0] = nO;
     }
-    if (nO == 0) {
-        // only the zero pad (none when nO == 0)
+    if (nO == 0)
         return;
+    // list the non-zero words once (one wave, ballot compaction), then
+    // visit (row, non-zero word) pairs only
+    int *nzw = reinterpret_cast<int *>(pre + nw);
+    if (tid < 64) {
+        int cnt = 0;
+        for (int base = 0; base < nw; base += 64) {
+            const int w = base + tid;
+            const bool nz = w < nw && bits[w] != 0u;
+            const uint64_t mask = __ballot(nz);
+            if (nz)
+                nzw[cnt + __popcll(mask & ((1ull << tid) - 1ull))] = w;
+            cnt += __popcll(mask);
+        }
+        if (tid == 0)
+            nnz_s = cnt;
     }
-    const int pairs = (n1 - n0) * nw;
+    __syncthreads();
+    const int nnz = nnz_s;
+    const int pairs = (n1 - n0) * nnz;
     for (int p = tid; p < pairs; p += kThreads) {
-        const int n = n0 + p / nw;
-        const int w = p - (p / nw) * nw;
+        const int n = n0 + p / nnz;
+        const int w = nzw[p - (p / nnz) * nnz];
         uint32_t b = bits[w];
-        if (!b)
-            continue;
         const int8_t *src = Wq + (int64_t)n * K + 32 * w;
         uint4 lo = *reinterpret_cast<const uint4 *>(src);
         uint4 hi = make_uint4(0, 0, 0, 0);
@@ -373,18 +494,22 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, uint16_t thr_mag,
     const int nchunk = (int)(K / 8);
     if (nchunk > 0) {
         const int gx = (nchunk + kThreads - 1) / kThreads;
-        // about 8 rows per block; more when T is huge (grid.y <= 65535)
-        int R = 8;
+        // rows per block: a multiple of the load batch, about 256
+        // workgroups in all (measured fastest), grid.y <= 65535
+        int gy = (int)std::min<int64_t>((T + kDetectRows - 1) / kDetectRows, std::max(1, 256 / gx));
+        int R = (int)((T + gy - 1) / gy);
+        R = (R + kDetectRows - 1) / kDetectRows * kDetectRows;
         while ((T + R - 1) / R > 65535)
             R *= 2;
-        const int gy = (int)((T + R - 1) / R);
+        gy = (int)((T + R - 1) / R);
         hipLaunchKernelGGL(k_detect, dim3(gx, gy), dim3(kThreads), 0, s, X, (int)T, (int)K,
                            R, (uint32_t)thr_mag, bits);
     }
-    const int wrows = 8;
+    const int wrows = 32;
     const int64_t wblocks = (N + wrows - 1) / wrows;
-    const size_t lds = 8 * (size_t)(nw > 0 ? nw : 1);
-    hipLaunchKernelGGL(k_prepare, dim3((unsigned)(T + wblocks)), dim3(kThreads), lds, s, X, Wq,
+    const size_t lds = 12 * (size_t)(nw > 0 ? nw : 1);   // bits, prefix, non-zero words
+    const int64_t xblocks = (T + kPrepRows - 1) / kPrepRows;
+    hipLaunchKernelGGL(k_prepare<kPrepRows>, dim3((unsigned)(xblocks + wblocks)), dim3(kThreads), lds, s, X, Wq,
                        (int)T, (int)K, (int)N, wrows, bits, meta,
                        reinterpret_cast<int32_t *>(ws + L.idx),
                        reinterpret_cast<float *>(ws + L.sX),
