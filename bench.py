@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--threshold", type=float, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables it)")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip timing the vendor int8 GEMM (torch._int_mm) for reference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -152,11 +154,38 @@ def main():
     prep_bytes = 2 * T * K + 2 * T * K + T * K + 4 * T + 2 * T * nO16 + 2 * N * nO16
     prep_gbps = prep_bytes / (prep_ms * 1e-3) / 1e9
 
+    reference = None
+    if not args.no_reference:
+        # context only: the vendor library's plain int8 GEMM (int32 output, no
+        # dequantization, no outlier columns) on the same shape and codes
+        Xq = st["Xq"]
+        WqT = Wq.t()
+        try:
+            for _ in range(5):
+                torch._int_mm(Xq, WqT)
+            torch.cuda.synchronize()
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            r0.record()
+            for _ in range(50):
+                torch._int_mm(Xq, WqT)
+            r1.record()
+            torch.cuda.synchronize()
+            ref_us = r0.elapsed_time(r1) / 50 * 1e3
+            reference = {"what": "torch._int_mm (hipBLASLt): int8 x int8 -> int32 only, same T, K, N",
+                         "us": round(ref_us, 2), "tops": round(ops / (ref_us * 1e-6) / 1e12, 1)}
+        except Exception as ex:  # the reference is optional context
+            reference = {"what": "torch._int_mm", "error": str(ex)[:200]}
+
     if args.copy_calibration:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        # one device-to-device copy of 1 GiB of initialized data (four
+        # times the last-level cache), whose true traffic is 1 GiB read +
+        # 1 GiB written: the scale for the HBM byte counters
+        a = torch.full((1 << 30,), 7, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
+        torch.cuda.synchronize()
         b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
     src = os.path.join(ROOT, "int8_matmul_amd", "csrc", "gemm.hip")
     out = {
@@ -179,6 +208,7 @@ def main():
         "gemm_us": round(gemm_ms * 1e3, 2),
         "quant_gbps": round(prep_gbps, 1),
         "quant_pct_hbm_peak": round(100.0 * prep_gbps / PEAK_HBM_GBPS, 2),
+        "vendor_int8_gemm": reference,
         "roofline": {
             "bound": "mfma",
             "kernel": "k_gemm (int8 MFMA GEMM + dequant/outlier epilogue)",
