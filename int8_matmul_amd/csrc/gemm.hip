@@ -47,6 +47,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 #define LI8_LDS __attribute__((address_space(3)))
 
 // Buffer resource over `bytes` bytes at p (raw buffer, offsets in bytes).
@@ -126,7 +127,9 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     // have every kernel argument the epilogue uses in registers before the
     // main loop: a scalar load in flight across it would make the compiler
     // wait for all LDS reads instead of the older half
-    asm volatile("" ::"s"(sX), "s"(sW), "s"(meta), "s"(XO), "s"(WO), "s"(Y), "s"(acc_out));
+    asm volatile("" ::"s"(sX), "s"(sW), "s"(XO), "s"(WO), "s"(Y), "s"(acc_out));
+    const int nO = meta[0];
+    asm volatile("" ::"s"(nO));
 
     // ---- global -> LDS loaders: load i of this lane fills LDS chunk
     // p = i*NT + wid*64 + lane of the stage (row p / CPR, physical chunk
@@ -196,12 +199,15 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
         for (int b = 0; b < FN; b++)
             fb[set][b] = *reinterpret_cast<const v4i *>(base + offB[b][kk]);
     };
+    // weight fragment first: acc[a][b] is the transposed block (features x
+    // tokens), which puts four consecutive output features in each group of
+    // four accumulator registers
     auto mfmas = [&](int set) {
 #pragma unroll
         for (int a = 0; a < FM; a++)
 #pragma unroll
             for (int b = 0; b < FN; b++)
-                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][a], fb[set][b], acc[a][b],
+                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[set][b], fa[set][a], acc[a][b],
                                                                  0, 0, 0);
     };
     // One stage.  WAIT: buffer loads allowed in flight at the barrier;
@@ -250,64 +256,145 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
         stage(kt, W0{}, TF{}, TT{});
 
     // ---- epilogue ----
-    // 32x32 MFMA result layout: lane l, register r -> column (l & 31),
-    // row 8*(r/4) + 4*(l/32) + (r%4) of the 32x32 block.
-    wait_loads_barrier<0>();   // the LDS is reused for the output staging
-    uint16_t *stg = reinterpret_cast<uint16_t *>(lds) + wid * (FM * 32) * RS;
-    const int nO = meta[0];
-    const int nch = (nO + 15) >> 4;
+    // acc[a][b], lane l, register r: token t = tok0 + 32a + (l & 31), feature
+    // n = fea0 + 32b + 8*(r/4) + (r%4), with tok0 / fea0 the first token and
+    // (for this half-wave) feature of the wave's sub-tile.
+    const int tok0 = m0 + wm * FM * 32 + (lane & 31);
+    const int fea0 = n0 + wn * FN * 32 + 4 * khalf;
+    if constexpr (STORE_ACC) {
 #pragma unroll
-    for (int a = 0; a < FM; a++) {
-        float sx[16];
+        for (int a = 0; a < FM; a++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int row = m0 + wm * FM * 32 + a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-            sx[r] = sX[min(row, T - 1)];
-        }
-        const int xrow = min(m0 + arow0 + a * 32, T - 1);
-#pragma unroll
-        for (int b = 0; b < FN; b++) {
-            if constexpr (STORE_ACC) {
-                const int col = n0 + wn * FN * 32 + b * 32 + (lane & 31);
+            for (int b = 0; b < FN; b++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const int row = m0 + wm * FM * 32 + a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-                    if (row < T && col < N)
-                        acc_out[(int64_t)row * N + col] = acc[a][b][r];
+                    const int t = tok0 + 32 * a, n = fea0 + 32 * b + 8 * (r >> 2) + (r & 3);
+                    if (t < T && n < N)
+                        acc_out[(int64_t)t * N + n] = acc[a][b][r];
                 }
-            }
-            v16f d;
+    }
+    // token scales and the first 16-column chunk of the outlier operands
+    // are requested together; the feature scales after the outlier loop
+    float sx[FM];
+#pragma unroll
+    for (int a = 0; a < FM; a++)
+        sx[a] = sX[min(tok0 + 32 * a, T - 1)];
+    // outlier operands, chunk c: lane l supplies 8 of the 16 columns
+    // (8*(l/32)..) of the weight row of block b and the token row of block
+    // a; buffer loads with a fixed per-lane offset and the chunk's offset
+    // in the scalar operand
+    const int nch = (nO + 15) >> 4;
+    const __amdgpu_buffer_rsrc_t rXO = make_rsrc(XO, (int)(2u * (unsigned)T * (unsigned)K));
+    const __amdgpu_buffer_rsrc_t rWO = make_rsrc(WO, N * K);
+    int voX[FM], voW[FN];
+#pragma unroll
+    for (int a = 0; a < FM; a++)
+        voX[a] = (int)((unsigned)min(tok0 + 32 * a, T - 1) * (unsigned)K * 2u + khalf * 16u);
+#pragma unroll
+    for (int b = 0; b < FN; b++)
+        voW[b] = min(n0 + wn * FN * 32 + 32 * b + (lane & 31), N - 1) * K + khalf * 8;
+    v8h ox[2][FM];
+    v2u ow[2][FN];
+    auto oload = [&](int set, int c) {
+#pragma unroll
+        for (int a = 0; a < FM; a++)
+            ox[set][a] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rXO, voX[a], c * 32, 0));
+#pragma unroll
+        for (int b = 0; b < FN; b++)
+            ow[set][b] = __builtin_amdgcn_raw_buffer_load_b64(rWO, voW[b], c * 16, 0);
+    };
+    if (nch > 0)
+        oload(0, 0);
+
+    // D = fl32(acc * sX)
+    v16f d[FM][FN];
+#pragma unroll
+    for (int a = 0; a < FM; a++)
+#pragma unroll
+        for (int b = 0; b < FN; b++)
 #pragma unroll
             for (int r = 0; r < 16; r++)
-                d[r] = (float)acc[a][b][r] * sx[r];
-            const int wcol = min(n0 + brow0 + b * 32, N - 1);
-            for (int c = 0; c < nch; c++) {
-                const v8h xa =
-                    *reinterpret_cast<const v8h *>(XO + (int64_t)xrow * K + c * 16 + khalf * 8);
-                const uint2 u =
-                    *reinterpret_cast<const uint2 *>(WO + (int64_t)wcol * K + c * 16 + khalf * 8);
-                const uint32_t w[2] = {u.x, u.y};
-                v8h wb;
+                d[a][b][r] = (float)acc[a][b][r] * sx[a];
+    // D += XO . WO^T over the outlier columns (codes are exact in fp16),
+    // the next chunk's loads in flight during this chunk's MFMAs
+    // `keep` is all ones, or zero for a chunk past the end (its codes are
+    // then masked to 0): the MFMAs run unconditionally so that the loads
+    // stay where they were issued, ahead of their use
+    auto omfma = [&](int set, uint32_t keep) {
+        v8h wb[FN];
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    wb[e] = (_Float16)(float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
-                d = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, wb, d, 0, 0, 0);
-            }
-            const int col = n0 + wn * FN * 32 + b * 32 + (lane & 31);
-            const float sw = sW[min(col, N - 1)];
+        for (int b = 0; b < FN; b++) {
+            const uint32_t w[2] = {ow[set][b][0] & keep, ow[set][b][1] & keep};
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                // fl32(D * sW) first, then one rounding to fp16: the empty
-                // asm keeps the compiler from fusing the product and the
-                // conversion into a single-rounding v_fma_mixlo_f16
-                float p = d[r] * sw;
-                asm("" : "+v"(p));
-                const _Float16 h = (_Float16)p;
-                stg[(a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3)) * RS + b * 32 + (lane & 31)] =
-                    __builtin_bit_cast(uint16_t, h);
-            }
+            for (int e = 0; e < 8; e++)
+                wb[b][e] = (_Float16)(float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
         }
+#pragma unroll
+        for (int a = 0; a < FM; a++)
+#pragma unroll
+            for (int b = 0; b < FN; b++)
+                d[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wb[b], ox[set][a], d[a][b], 0, 0, 0);
+    };
+    // two chunks per iteration; a chunk index past the end re-reads the
+    // last chunk (a valid address) and is masked
+    // (the scheduling barriers keep the compiler from moving the loads
+    // down next to their use)
+    for (int c = 0; c < nch; c += 2) {
+        oload(1, min(c + 1, nch - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        omfma(0, ~0u);
+        __builtin_amdgcn_sched_barrier(0);
+        oload(0, min(c + 2, nch - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        omfma(1, (c + 1 < nch) ? ~0u : 0u);
+        __builtin_amdgcn_sched_barrier(0);
     }
+
+    float4 sw[FN][4];
+    if ((N & 3) == 0) {   // 16-byte loads; a group starting below N ends below N
+#pragma unroll
+        for (int b = 0; b < FN; b++)
+#pragma unroll
+            for (int g = 0; g < 4; g++)
+                sw[b][g] = *reinterpret_cast<const float4 *>(sW + min(fea0 + 32 * b + 8 * g, N - 4));
+    } else {
+#pragma unroll
+        for (int b = 0; b < FN; b++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int n = fea0 + 32 * b + 8 * g;
+                sw[b][g].x = sW[min(n, N - 1)];
+                sw[b][g].y = sW[min(n + 1, N - 1)];
+                sw[b][g].z = sW[min(n + 2, N - 1)];
+                sw[b][g].w = sW[min(n + 3, N - 1)];
+            }
+    }
+    // Y = fp16(fl32(D * sW)), four consecutive features per 8-byte LDS write
+    // into the wave's staging rows (one row per token).  The ring buffers
+    // are reused for the staging: every wave must be done reading them.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    uint16_t *stg = reinterpret_cast<uint16_t *>(lds) + wid * (FM * 32) * RS;
+#pragma unroll
+    for (int a = 0; a < FM; a++)
+#pragma unroll
+        for (int b = 0; b < FN; b++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const float s4[4] = {sw[b][g].x, sw[b][g].y, sw[b][g].z, sw[b][g].w};
+                uint32_t h[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    // fl32(D * sW) first, then one rounding to fp16: the
+                    // empty asm keeps the compiler from fusing the product
+                    // and the conversion into a single-rounding
+                    // v_fma_mixlo_f16
+                    float p = d[a][b][4 * g + j] * s4[j];
+                    asm("" : "+v"(p));
+                    h[j] = __builtin_bit_cast(uint16_t, (_Float16)p);
+                }
+                *reinterpret_cast<uint2 *>(stg + (a * 32 + (lane & 31)) * RS + b * 32 + 8 * g +
+                                           4 * khalf) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
     // each wave stores its own sub-tile (only its own LDS rows: no barrier)
     constexpr int CPRW = FN * 32 / 8;   // 16-byte chunks per sub-tile row
     constexpr int NCH = FM * 32 * CPRW;
