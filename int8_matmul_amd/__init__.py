@@ -29,7 +29,7 @@ import torch
 __all__ = [
     "Int8MatmulError", "LibraryNotBuilt", "library_path", "load_library",
     "quantize_weight", "workspace_bytes", "new_workspace", "linear", "prepare",
-    "gemm", "export_stages", "STATUS",
+    "gemm", "export_stages", "few_token_path", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +44,17 @@ STATUS = {
     4: "LI8_ERR_WORKSPACE",
     5: "LI8_ERR_HIP",
 }
+
+
+# Shapes the library runs on its few-token path: ``linear`` is one fused
+# kernel there (kDecodeMaxT / kDecodeMaxK in csrc/li8_internal.h).
+FEW_TOKEN_MAX_T = 16
+FEW_TOKEN_MAX_K = 8192
+
+
+def few_token_path(T: int, K: int) -> bool:
+    """True if ``linear`` runs as the single fused few-token kernel for T x K."""
+    return 1 <= T <= FEW_TOKEN_MAX_T and 16 <= K <= FEW_TOKEN_MAX_K
 
 
 class Int8MatmulError(RuntimeError):

@@ -158,6 +158,9 @@ li8_status llm_int8_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     const WsLayout L = ws_layout(T, K, N);
+    if (decode_shape(T, K))
+        return from_hip(launch_decode_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), acc,
+                                           static_cast<const char *>(workspace), L, stream));
     return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), acc,
                                 static_cast<const char *>(workspace), L, stream));
 }
@@ -171,6 +174,11 @@ li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW, flo
         st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
+    // few tokens: one kernel, bit-identical to the prepare + gemm pair
+    if (decode_shape(T, K))
+        return from_hip(launch_decode_fused(static_cast<const uint16_t *>(X), Wq, sW,
+                                            threshold_magnitude(threshold), T, K, N,
+                                            static_cast<uint16_t *>(Y), stream));
     const WsLayout L = ws_layout(T, K, N);
     hipError_t e = launch_prepare(static_cast<const uint16_t *>(X), Wq,
                                   threshold_magnitude(threshold), T, K, N,

@@ -1,0 +1,500 @@
+// The LLM.int8() layer for few tokens (decode: T <= 16), for gfx950.
+//
+// Same arithmetic as the prepare kernels followed by the tiled GEMM:
+//   O       = { j : some |X[t,j]| > threshold }                (union over t)
+//   sX[t]   = fl32(max_{j not in O} |X[t,j]| / 127), Xq codes rne, 0 on O
+//   acc     = sum_j Xq[t,j] Wq[n,j]                            (exact int32)
+//   D       = fl32(acc * sX[t]) + sum_{j in O} X[t,j] Wq[n,j]  (fp16 MFMA, fp32)
+//   Y[t,n]  = fp16(fl32(D * sW[n]))
+// (hncyxsy.com/news/230290, section 2.1: outlier columns in fp16, the rest
+// in int8 with row and column scales, the two products added in fp16;
+// tqpw.cn/news/5683, section 2.1: absmax scales and codes.)
+//
+// With T <= 16 the layer is bound by reading Wq (N*K bytes) from HBM once;
+// every other operand is a few KB.  So the whole call is one kernel:
+//  - Each workgroup handles 16-feature row groups (a grid-stride loop).
+//    Its first batch of Wq loads is issued at entry, so that the HBM
+//    latency overlaps the activation work below.
+//  - The activation work: every workgroup reads the T rows of X (L2
+//    resident after the first), finds the outlier columns, the row scales
+//    and the codes itself, and keeps the codes in LDS.  This is redundant
+//    across workgroups, and it avoids three dependent launches.
+//  - Per row group, the 8 waves split K; each wave multiplies 16 weight
+//    rows (MFMA A operand, straight from global memory) by the token codes
+//    (B operand, 16 token slots, from LDS) with v_mfma_i32_16x16x64_i8.
+//    The int32 partial sums are added across waves in LDS (exact, so the
+//    order does not matter).
+//  - Wave 0 finishes the row group: dequantization, the outlier product as
+//    v_mfma_f32_16x16x32_f16 over chunks of 32 outlier columns (gathered
+//    from X and Wq by column index), the column scale and the fp16 store.
+// The variant FUSED = false reads the token codes, scales and outlier
+// columns that the prepare kernels left in the workspace instead of
+// deriving them; everything after that is the same code, so the two
+// variants give bit-identical results.
+#include "li8_internal.h"
+#include "quant_math.h"
+
+namespace li8 {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int kDThreads = 512;   // 8 waves, two per SIMD
+constexpr int kDWaves = kDThreads / 64;
+constexpr int kDRows = 16;       // output features per row group
+constexpr int kDMaxT = kDecodeMaxT;
+constexpr int kDMaxK = kDecodeMaxK;
+constexpr int kOutOfRange = (int)0x80000000;   // buffer offset past any operand
+
+// LDS carve-up (bytes).  Token codes: block q (columns 16q..16q+15) holds
+// the 16 codes of token t at q*QS + 16t, QS = 16T + 16 (the 16-byte pad
+// spreads the writes of consecutive blocks over the banks).
+constexpr int kXqMax = kDMaxK / 16 * (16 * kDMaxT + 16);
+constexpr int kOffBits = kXqMax;                          // uint32[K/32]
+constexpr int kOffPre = kOffBits + 4 * (kDMaxK / 32);     // int32[K/32]
+constexpr int kOffRmax = kOffPre + 4 * (kDMaxK / 32);     // uint32[8][16]
+constexpr int kOffSx = kOffRmax + 4 * kDWaves * kDMaxT;   // float[16] token scales
+constexpr int kOffRx = kOffSx + 4 * kDMaxT;               // float[16] their reciprocals
+constexpr int kOffRed = kOffRx + 4 * kDMaxT;              // v4i[2][8][64]
+constexpr int kIdxCap = 1024;                             // outlier columns listed in LDS
+constexpr int kOffIdx = kOffRed + 2 * kDWaves * 64 * 16;  // int32[kIdxCap]
+constexpr int kLds = kOffIdx + 4 * kIdxCap;
+static_assert(kLds <= 160 * 1024, "LDS of one workgroup");
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+// 16 bytes of Wq at byte offset `off` (kOutOfRange reads zeros).
+__device__ __forceinline__ v4i load_w16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Columns of the outlier set with ranks i0 .. i0+7 (ascending), from the
+// bit set and the exclusive prefix counts of its words; -1 past nO.
+__device__ void outlier_columns8(const uint32_t *bits, const int32_t *pre, int nw, int nO, int i0,
+                                 int col[8])
+{
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        col[e] = -1;
+    if (i0 >= nO)
+        return;
+    // the word holding rank i0: the last word whose prefix is <= i0
+    int lo = 0, hi = nw - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= i0)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int w = lo;
+    uint32_t b = bits[w];
+    for (int s = i0 - pre[w]; s > 0; s--)
+        b &= b - 1u;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        if (i0 + e >= nO)
+            break;
+        col[e] = 32 * w + __ffs(b) - 1;
+        b &= b - 1u;
+        while (b == 0u && w + 1 < nw)
+            b = bits[++w];
+    }
+}
+
+template <bool FUSED, int KB, bool STORE_ACC>
+__global__ __launch_bounds__(kDThreads) void k_decode(
+    const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq, const float *__restrict__ sW,
+    uint32_t thr_mag, int T, int K, int N,
+    const int32_t *__restrict__ meta, const int32_t *__restrict__ idx_g,
+    const float *__restrict__ sX_g, const int8_t *__restrict__ Xq_g,
+    const uint16_t *__restrict__ XO_g, uint16_t *__restrict__ Y, int32_t *__restrict__ acc_out)
+{
+    __shared__ __attribute__((aligned(16))) int8_t lds[kLds];
+    int8_t *xq = lds;
+    uint32_t *bits = reinterpret_cast<uint32_t *>(lds + kOffBits);
+    int32_t *pre = reinterpret_cast<int32_t *>(lds + kOffPre);
+    uint32_t *rmax = reinterpret_cast<uint32_t *>(lds + kOffRmax);
+    float *sxl = reinterpret_cast<float *>(lds + kOffSx);
+    float *rxl = reinterpret_cast<float *>(lds + kOffRx);
+    int32_t *idxl = reinterpret_cast<int32_t *>(lds + kOffIdx);
+    v4i *red = reinterpret_cast<v4i *>(lds + kOffRed);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int QS = 16 * T + 16;
+    const int NRG = (N + kDRows - 1) / kDRows;
+    const int G = gridDim.x;
+
+    // ---- this wave's share of K: MFMA k-steps [s0, s1) of 64 columns ----
+    const int S = (K + 63) / 64;
+    const int s0 = wid * S / kDWaves, s1 = (wid + 1) * S / kDWaves;
+    const int kg = lane >> 4;     // 16-byte group of the k-step this lane supplies
+    const int tok = lane & 15;    // token slot (B column) of this lane
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wq, N * K);
+
+    v4i wbuf[2][KB];
+    auto wload = [&](int set, int rg) {
+        const int n = min(rg * kDRows + (lane & 15), N - 1);
+#pragma unroll
+        for (int j = 0; j < KB; j++) {
+            const int k = (s0 + j) * 64 + 16 * kg;
+            wbuf[set][j] = load_w16(rW, (s0 + j < s1 && k < K) ? n * K + k : kOutOfRange);
+        }
+    };
+    int rg = blockIdx.x;
+
+    // ---- token codes, scales, outlier set ----
+    // The activation loads are issued before the first weight batch: loads
+    // complete in order, so this way the activation work waits only for
+    // its own data while the weight batch is in flight.  (The fused
+    // variant with two chunks of X per thread has no registers to spare
+    // for the weights during that work: it requests them after it.)
+    constexpr bool kEarly = !(FUSED && KB > 8);
+    int nO;
+    if constexpr (FUSED) {
+        constexpr int CPT = KB / 8;   // 8-column chunks per thread: K <= 4096*CPT
+        const int nchunk = K / 8;
+        const int nw = (K + 31) / 32;
+        const uint4 *x4 = reinterpret_cast<const uint4 *>(X);
+        uint4 xv[CPT][kDMaxT];
+#pragma unroll
+        for (int u = 0; u < CPT; u++) {
+            const int c = tid + u * kDThreads;
+#pragma unroll
+            for (int t = 0; t < kDMaxT; t++) {
+                xv[u][t] = make_uint4(0, 0, 0, 0);
+                if (t < T && c < nchunk)
+                    xv[u][t] = x4[(int64_t)t * (K / 8) + c];
+            }
+        }
+        if (kEarly && rg < NRG)
+            wload(0, rg);
+        uint32_t fl[CPT];
+        uint32_t rm[kDMaxT];
+#pragma unroll
+        for (int t = 0; t < kDMaxT; t++)
+            rm[t] = 0;
+#pragma unroll
+        for (int u = 0; u < CPT; u++) {
+            const int c = tid + u * kDThreads;
+            li8_us2 mx[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+#pragma unroll
+            for (int t = 0; t < kDMaxT; t++)
+                column_max8(mx, xv[u][t]);   // padding rows are zero
+            fl[u] = outlier_flags8(mx, thr_mag);
+            // chunks 4w..4w+3 sit in four consecutive lanes: one word
+            uint32_t word = fl[u] << (8 * (c & 3));
+            word |= (uint32_t)__shfl_xor((int)word, 1, 64);
+            word |= (uint32_t)__shfl_xor((int)word, 2, 64);
+            if ((c & 3) == 0 && c < nchunk)
+                bits[c >> 2] = word;
+#pragma unroll
+            for (int t = 0; t < kDMaxT; t++)
+                rm[t] = max(rm[t], chunk_max(xv[u][t], fl[u]));
+        }
+        // all reductions first (they overlap), then the stores
+        uint32_t wm[kDMaxT];
+#pragma unroll
+        for (int t = 0; t < kDMaxT; t++)
+            wm[t] = wave_max(rm[t]);
+        if (lane < kDMaxT) {
+            uint32_t m = wm[0];
+#pragma unroll
+            for (int t = 1; t < kDMaxT; t++)
+                m = (lane == t) ? wm[t] : m;
+            rmax[wid * kDMaxT + lane] = m;
+        }
+        lds_barrier();
+        // one thread per token: its scale and the reciprocal (IEEE
+        // divisions), shared through LDS
+        if (tid < kDMaxT) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int w = 0; w < kDWaves; w++)
+                m = max(m, rmax[w * kDMaxT + tid]);
+            const float sc = h2f(m) / 127.0f;
+            sxl[tid] = sc;
+            rxl[tid] = 1.0f / sc;
+        }
+        lds_barrier();
+        float sx[kDMaxT], rx[kDMaxT];
+#pragma unroll
+        for (int t = 0; t < kDMaxT; t++) {
+            sx[t] = sxl[t];
+            rx[t] = rxl[t];
+        }
+#pragma unroll
+        for (int u = 0; u < CPT; u++) {
+            const int c = tid + u * kDThreads;
+            if (c < nchunk) {
+#pragma unroll
+                for (int t = 0; t < kDMaxT; t++)
+                    if (t < T) {
+                        const uint2 q = (sx[t] == 0.0f) ? make_uint2(0u, 0u)
+                                                        : token_codes8(xv[u][t], fl[u], sx[t], rx[t]);
+                        *reinterpret_cast<uint2 *>(xq + (c >> 1) * QS + 16 * t + 8 * (c & 1)) = q;
+                    }
+            }
+        }
+        lds_barrier();
+        // exclusive prefix counts of the bit-set words, for the outlier
+        // column ranks (only wave 0 uses them)
+        nO = 0;
+        if (wid == 0) {
+            const int per = (nw + 63) / 64;
+            const int w0 = min(nw, lane * per), w1 = min(nw, w0 + per);
+            int cnt = 0;
+            for (int w = w0; w < w1; w++)
+                cnt += __popc(bits[w]);
+            // exclusive prefix of cnt (< 256) over the lanes, bit by bit
+            // with ballots: no LDS round trips
+            const uint64_t below = (1ull << lane) - 1ull;
+            int p = 0;
+            nO = 0;
+#pragma unroll
+            for (int bit = 0; bit < 8; bit++) {
+                const uint64_t m = __ballot((cnt >> bit) & 1);
+                p += __popcll(m & below) << bit;
+                nO += __popcll(m) << bit;
+            }
+            for (int w = w0; w < w1; w++) {
+                pre[w] = p;
+                uint32_t b = bits[w];
+                if (nO <= kIdxCap)   // the ascending list of outlier columns
+                    while (b) {
+                        idxl[p++] = 32 * w + __ffs(b) - 1;
+                        b &= b - 1u;
+                    }
+                else
+                    p += __popc(b);
+            }
+        }
+    } else {
+        // token codes of the prepared workspace into the LDS layout: up to
+        // 16 chunks of 16 bytes per thread (T*K/16 <= 16*512)
+        nO = meta[0];
+        const int nq = K / 16, tot = T * nq;
+        uint4 st[kDMaxT];
+#pragma unroll
+        for (int j = 0; j < kDMaxT; j++) {
+            const int i = tid + j * kDThreads;
+            if (i < tot) {
+                const int t = i / nq, q = i - t * nq;
+                st[j] = *reinterpret_cast<const uint4 *>(Xq_g + (int64_t)t * K + 16 * q);
+            }
+        }
+        if (rg < NRG)
+            wload(0, rg);
+#pragma unroll
+        for (int j = 0; j < kDMaxT; j++) {
+            const int i = tid + j * kDThreads;
+            if (i < tot) {
+                const int t = i / nq, q = i - t * nq;
+                *reinterpret_cast<uint4 *>(xq + q * QS + 16 * t) = st[j];
+            }
+        }
+        if (tid < kDMaxT)
+            sxl[tid] = tid < T ? sX_g[tid] : 0.0f;
+        lds_barrier();
+    }
+
+    if (!kEarly && rg < NRG)
+        wload(0, rg);
+
+    // ---- row groups: int8 MFMAs over this wave's share of K ----
+    // Outlier operands of 8 consecutive ranks from i0 for this lane, in two
+    // steps so that the loads can be in flight across a barrier: the raw
+    // values (weight code of row wrow, binary16 of token tok; clamped,
+    // always valid addresses), then the MFMA fragments with the ranks past
+    // nO (and padding tokens) zeroed.
+    auto gather_raw = [&](int wrow, int i0, int (&wr)[8], uint32_t (&xr)[8]) {
+        int col[8];
+        if constexpr (FUSED) {
+            if (nO <= kIdxCap) {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    col[e] = (i0 + e < nO) ? idxl[i0 + e] : 0;
+            } else {   // more columns than the LDS list holds
+                outlier_columns8(bits, pre, (K + 31) / 32, nO, i0, col);
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    col[e] = max(col[e], 0);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                col[e] = (i0 + e < nO) ? idx_g[i0 + e] : 0;
+        }
+        const int64_t trow = (int64_t)min(tok, T - 1) * K;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            wr[e] = Wq[(int64_t)wrow * K + col[e]];
+            xr[e] = FUSED ? X[trow + col[e]] : XO_g[trow + ((i0 + e < nO) ? i0 + e : 0)];
+        }
+    };
+    auto fragments = [&](int i0, const int (&wr)[8], const uint32_t (&xr)[8], v8h &a, v8h &b) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const bool ok = i0 + e < nO;
+            a[e] = ok ? (_Float16)(float)wr[e] : (_Float16)0.0f;
+            b[e] = (ok && tok < T) ? __builtin_bit_cast(_Float16, (uint16_t)xr[e]) : (_Float16)0.0f;
+        }
+    };
+
+    auto process = [&](int set, int rgc, int par) {
+        // wave 0 requests its feature scales first, so that they arrive
+        // during the MFMAs
+        const int nb = rgc * kDRows + 4 * kg;   // this lane's first feature
+        const int wrow = min(rgc * kDRows + (lane & 15), N - 1);
+        float swv[4];
+        if (wid == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                swv[r] = sW[min(nb + r, N - 1)];
+        }
+        v4i acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < KB; j++) {
+            const int q = (s0 + j) * 4 + kg;
+            v4i xf = {0, 0, 0, 0};
+            if (tok < T && s0 + j < s1 && 16 * q < K)
+                xf = *reinterpret_cast<const v4i *>(xq + q * QS + 16 * tok);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbuf[set][j], xf, acc, 0, 0, 0);
+        }
+        // wave 0 requests the first 32 outlier columns before the barrier
+        int wr0[8];
+        uint32_t xr0[8];
+        if (wid == 0 && nO > 0)
+            gather_raw(wrow, 8 * kg, wr0, xr0);
+        red[(par * kDWaves + wid) * 64 + lane] = acc;
+        lds_barrier();
+        if (wid != 0)
+            return;
+        // wave 0: lane holds token tok and features nb .. nb+3
+        v4i tot = red[par * kDWaves * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < kDWaves; w++)
+            tot += red[(par * kDWaves + w) * 64 + lane];
+        if constexpr (STORE_ACC) {
+            if (tok < T)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    if (nb + r < N)
+                        acc_out[(int64_t)tok * N + nb + r] = tot[r];
+        }
+        const float sx = sxl[tok];
+        v4f d;
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            d[r] = (float)tot[r] * sx;
+        // D += X[:, O] . Wq[:, O]^T, 32 outlier columns per MFMA: lane
+        // supplies weight row (lane & 15) and token tok at ranks
+        // 32c + 8*kg .. +7
+        for (int c = 0; c < (nO + 31) / 32; c++) {
+            const int i0 = 32 * c + 8 * kg;
+            v8h a, b;
+            if (c == 0) {
+                fragments(i0, wr0, xr0, a, b);
+            } else {
+                int wr[8];
+                uint32_t xr[8];
+                gather_raw(wrow, i0, wr, xr);
+                fragments(i0, wr, xr, a, b);
+            }
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, d, 0, 0, 0);
+        }
+        if (tok >= T)
+            return;
+        uint32_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            // fl32(D * sW) first, then one rounding to fp16 (the empty asm
+            // keeps the product and the conversion from being fused)
+            float p = d[r] * swv[r];
+            asm("" : "+v"(p));
+            h[r] = __builtin_bit_cast(uint16_t, (_Float16)p);
+        }
+        uint16_t *y = Y + (int64_t)tok * N + nb;
+        if ((N & 3) == 0 && nb + 3 < N) {
+            *reinterpret_cast<uint2 *>(y) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                if (nb + r < N)
+                    y[r] = (uint16_t)h[r];
+        }
+    };
+
+    // two row groups per iteration, so that the register set holding the
+    // next group's weights is fixed at compile time; the next group's loads
+    // are issued before this group's MFMAs
+    while (rg < NRG) {
+        const int rg1 = rg + G;
+        if (rg1 < NRG)
+            wload(1, rg1);
+        process(0, rg, 0);
+        if (rg1 >= NRG)
+            break;
+        const int rg2 = rg1 + G;
+        if (rg2 < NRG)
+            wload(0, rg2);
+        process(1, rg1, 1);
+        rg = rg2;
+    }
+}
+
+template <bool FUSED, int KB>
+hipError_t launch_kb(const uint16_t *X, const int8_t *Wq, const float *sW, uint32_t thr_mag,
+                     int64_t T, int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
+                     const WsLayout &L, hipStream_t s)
+{
+    const int nrg = (int)((N + kDRows - 1) / kDRows);
+    const dim3 grid((unsigned)(nrg < kDecodeMaxBlocks ? nrg : kDecodeMaxBlocks));
+    const int32_t *meta = FUSED ? nullptr : reinterpret_cast<const int32_t *>(ws + L.meta);
+    const int32_t *idx = FUSED ? nullptr : reinterpret_cast<const int32_t *>(ws + L.idx);
+    const float *sX = FUSED ? nullptr : reinterpret_cast<const float *>(ws + L.sX);
+    const int8_t *Xq = FUSED ? nullptr : reinterpret_cast<const int8_t *>(ws + L.Xq);
+    const uint16_t *XO = FUSED ? nullptr : reinterpret_cast<const uint16_t *>(ws + L.XO);
+    if (acc)
+        hipLaunchKernelGGL((k_decode<FUSED, KB, true>), grid, dim3(kDThreads), 0, s, X, Wq, sW,
+                           thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
+    else
+        hipLaunchKernelGGL((k_decode<FUSED, KB, false>), grid, dim3(kDThreads), 0, s, X, Wq, sW,
+                           thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
+    return hipGetLastError();
+}
+
+} // namespace
+
+bool decode_shape(int64_t T, int64_t K)
+{
+    return T >= 1 && T <= kDecodeMaxT && K >= 16 && K <= kDecodeMaxK;
+}
+
+hipError_t launch_decode_fused(const uint16_t *X, const int8_t *Wq, const float *sW,
+                               uint16_t thr_mag, int64_t T, int64_t K, int64_t N, uint16_t *Y,
+                               hipStream_t s)
+{
+    static const WsLayout none{};
+    if (K <= 4096)
+        return launch_kb<true, 8>(X, Wq, sW, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
+    return launch_kb<true, 16>(X, Wq, sW, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
+}
+
+hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
+                              uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L,
+                              hipStream_t s)
+{
+    if (K <= 4096)
+        return launch_kb<false, 8>(nullptr, Wq, sW, 0, T, K, N, Y, acc, ws, L, s);
+    return launch_kb<false, 16>(nullptr, Wq, sW, 0, T, K, N, Y, acc, ws, L, s);
+}
+
+} // namespace li8

@@ -16,6 +16,12 @@ constexpr int64_t kMaxOperandBytes = ((int64_t)1 << 31) - 1;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Few-token path (one fused kernel): T <= kDecodeMaxT token rows, whose
+// codes for all of K stay in LDS, hence the bound on K.
+constexpr int kDecodeMaxT = 16;
+constexpr int kDecodeMaxK = 8192;
+constexpr int kDecodeMaxBlocks = 256;   // one workgroup per CU
+
 // Device workspace carved into fixed regions.  Offsets depend only on the
 // shape (T, K, N), never on the data, so the host needs no readback.
 //   bits : uint32[ceil(K/32)]  outlier column bit set (cleared every call)
@@ -59,5 +65,16 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, uint16_t thr_mag,
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K,
                        int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
                        const WsLayout &L, hipStream_t s);
+
+// Few-token path (decode.hip).  decode_shape(T, K) says whether both
+// entry points use it for this shape; the fused launch does the whole
+// layer from X, the other reads what launch_prepare left in the workspace.
+bool decode_shape(int64_t T, int64_t K);
+hipError_t launch_decode_fused(const uint16_t *X, const int8_t *Wq, const float *sW,
+                               uint16_t thr_mag, int64_t T, int64_t K, int64_t N, uint16_t *Y,
+                               hipStream_t s);
+hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
+                              uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L,
+                              hipStream_t s);
 
 } // namespace li8

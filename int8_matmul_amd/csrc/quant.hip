@@ -21,47 +21,13 @@
 #include <algorithm>
 
 #include "li8_internal.h"
+#include "quant_math.h"
 
 namespace li8 {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPrepRows = 2;   // token rows per quantization workgroup
-
-__device__ __forceinline__ float h2f(uint32_t h)
-{
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
-// Quotient fl32(x / s) without a per-element division: with r = fl32(1/s)
-// computed once per vector, q0 = fl32(x*r), the residual e = x - q0*s is
-// exact as an fma, and fl32(q0 + e*r) is the correctly rounded quotient.
-// This is Markstein's correction step; for this kernel's inputs (s =
-// fl32(a/127) for an fp16 absmax a, x fp16 with |x| <= a) it has been
-// checked bit-exact against IEEE division over every such pair.
-__device__ __forceinline__ float quotient(float x, float s, float r)
-{
-    const float q0 = x * r;
-    const float e = fmaf(-q0, s, x);
-    return fmaf(e, r, q0);
-}
-
-// Code of one value for a row scale s > 0 with r = fl32(1/s): round half to
-// even of the fp32 quotient, clamped to [-127, 127].
-__device__ __forceinline__ int code_of(uint32_t h, float s, float r)
-{
-    float q = rintf(quotient(h2f(h), s, r));
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (int)q;
-}
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
-}
 
 // Block-wide max of a uint32 (all threads get the result).
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *red)
@@ -77,22 +43,6 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *red)
         r = max(r, red[i]);
     __syncthreads();
     return r;
-}
-
-// Max magnitude of the 8 binary16 values in v whose bit in `skip` is clear.
-__device__ __forceinline__ uint32_t masked_max8(uint4 v, uint32_t skip)
-{
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
-        if (!((skip >> (2 * i)) & 1u))
-            m = max(m, lo);
-        if (!((skip >> (2 * i + 1)) & 1u))
-            m = max(m, hi);
-    }
-    return m;
 }
 
 // Codes of 8 values packed little-endian into two words; positions whose
@@ -159,7 +109,7 @@ __global__ void k_clear(uint32_t *__restrict__ bits, int nwords, int32_t *__rest
 // combine their 8-bit masks into one 32-bit word, and non-zero words are
 // OR-ed into the bit set.
 // ---------------------------------------------------------------------------
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef li8_us2 us2;
 
 constexpr int kDetectRows = 16;   // rows per load batch
 
@@ -181,21 +131,11 @@ __global__ __launch_bounds__(kThreads) void k_detect(
             for (int u = 0; u < kDetectRows; u++)
                 v[u] = p[(int64_t)min(tb + u, t1 - 1) * stride];
 #pragma unroll
-            for (int u = 0; u < kDetectRows; u++) {
-                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    mx[i] = __builtin_elementwise_max(
-                        mx[i], __builtin_bit_cast(us2, w[i] & 0x7fff7fffu));
-            }
+            for (int u = 0; u < kDetectRows; u++)
+                column_max8(mx, v[u]);
         }
     }
-    uint32_t m8 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        m8 |= ((uint32_t)mx[i].x > thr_mag ? 1u : 0u) << (2 * i);
-        m8 |= ((uint32_t)mx[i].y > thr_mag ? 1u : 0u) << (2 * i + 1);
-    }
+    const uint32_t m8 = outlier_flags8(mx, thr_mag);
     // chunk c holds columns 8c..8c+7 = bits 8*(c%4).. of word c/4
     uint32_t word = m8 << (8 * (c & 3));
     word |= (uint32_t)__shfl_xor((int)word, 1, 64);
@@ -251,52 +191,6 @@ __device__ int load_bits_and_scan(const uint32_t *__restrict__ bits_g, int nw,
 // wrows rows of Wq each.  Every block rebuilds the prefix counts of the bit
 // set in LDS, which gives each outlier column its compact index.
 // ---------------------------------------------------------------------------
-
-// Code byte of one value for a row scale s > 0 (r = fl32(1/s)), in the low
-// byte of the result.  Adding 1.5 * 2^23 rounds the quotient half-to-even
-// to an integer held in the low mantissa bits (two's complement), and
-// |code| <= 127 holds for every |x| <= absmax, so no clamp is needed; both
-// facts, like the quotient itself, are checked over every possible input.
-__device__ __forceinline__ uint32_t code_bits(uint32_t h, float s, float r)
-{
-    return __builtin_bit_cast(uint32_t, quotient(h2f(h), s, r) + 12582912.0f);
-}
-
-// Low bytes of four words packed into one (v_perm_b32 byte selects).
-__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
-{
-    return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
-}
-
-// Codes of the 8 values of a 16-byte chunk; positions set in `skip` (outlier
-// columns) get code 0.
-__device__ __forceinline__ uint2 token_codes8(uint4 v, uint32_t skip, float s, float r)
-{
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t c[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++)
-        c[e] = code_bits((w[e >> 1] >> (16 * (e & 1))) & 0xffffu, s, r);
-    if (skip) {
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            if ((skip >> e) & 1u)
-                c[e] = 0u;
-    }
-    return make_uint2(pack_low_bytes(c[0], c[1], c[2], c[3]), pack_low_bytes(c[4], c[5], c[6], c[7]));
-}
-
-// Max magnitude of the 8 values of a chunk, skipping positions set in skip.
-__device__ __forceinline__ uint32_t chunk_max(uint4 v, uint32_t skip)
-{
-    if (skip)
-        return masked_max8(v, skip);
-    us2 m = __builtin_elementwise_max(__builtin_bit_cast(us2, v.x & 0x7fff7fffu),
-                                      __builtin_bit_cast(us2, v.y & 0x7fff7fffu));
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v.z & 0x7fff7fffu));
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v.w & 0x7fff7fffu));
-    return max((uint32_t)m.x, (uint32_t)m.y);
-}
 
 template <int ROWS>
 __global__ __launch_bounds__(kThreads) void k_prepare(

@@ -144,6 +144,37 @@ def test_ragged_shapes(T, K, N, thr):
     check_full(X, W, thr, f"ragged {T}x{K}x{N}")
 
 
+# T <= 16 and K <= 8192 take the few-token path (one fused kernel for
+# linear, a kernel reading the prepared workspace for gemm).
+@pytest.mark.parametrize("T,K,N", [
+    (1, 4096, 4101),     # one token; the last 16-feature row group holds 5 features
+    (3, 48, 17),         # K not a multiple of 64: the last MFMA k-step is part padding
+    (8, 4112, 300),      # K just above 4096: two 8-column chunks of X per thread
+    (16, 8192, 130),     # the largest few-token shape
+    (15, 1024, 1),       # a single output feature
+    (16, 16, 33),        # one 16-column block of K
+])
+@pytest.mark.parametrize("thr", [6.0, np.inf, 0.0])
+def test_decode_shapes(T, K, N, thr):
+    w = workloads.WORKLOADS["decode_7b_attn"]
+    rng = np.random.default_rng(T * 11 + K * 5 + N)
+    X, _ = workloads.make_activation(w, seed=int(rng.integers(1 << 30)), T=T, K=K)
+    W = workloads.make_weight(w, seed=int(rng.integers(1 << 30)), N=N, K=K)
+    check_full(X, W, thr, f"decode {T}x{K}x{N}")
+
+
+def test_decode_many_outliers():
+    """Several 32-column chunks of outliers spread over many bit-set words,
+    on the few-token path."""
+    w = workloads.WORKLOADS["ffn_13b"]
+    import dataclasses
+    w = dataclasses.replace(w, T=8, K=5120, N=200, sparse_rate=5e-3)
+    X, _ = workloads.make_activation(w)
+    W = workloads.make_weight(w)
+    g, o = check_full(X, W, 6.0, "decode many outliers")
+    assert o["nO"] > 150
+
+
 def test_many_outliers_13b_like():
     """Hundreds of outlier columns (token-sparse outliers as in the 13B
     workload, at a higher rate) on a reduced shape."""
@@ -245,6 +276,7 @@ def test_full_size_sampled(name):
     Wq, sW = li8.quantize_weight(Wd)
     ws = li8.new_workspace(T, K, N, DEV)
     Y = li8.linear(Xd, Wq, sW, w.threshold, workspace=ws)   # the call the benchmark times
+    li8.prepare(Xd, Wq, w.threshold, ws)   # the stages are defined by a prepare call
     st = li8.export_stages(ws, T, K, N)
     acc = torch.empty((T, N), dtype=torch.int32, device=DEV)
     Y2 = li8.gemm(Wq, sW, T, ws, acc=acc)
