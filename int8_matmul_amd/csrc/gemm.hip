@@ -446,9 +446,23 @@ hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, i
 
 } // namespace
 
+// Tile shape: 256x256 by default; 256x128 (8 waves of 64x64) when the
+// 256x256 grid leaves a large part of the last round of workgroups empty
+// (few tokens per 256 rows, or a tile count just above a multiple of the
+// CU count).  Cost model: rounds of workgroups over the 256 CUs times the
+// work of one tile, the smaller tile charged 10 % more per operation for
+// its lower reuse.
+constexpr int kCUs = 256;
+
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
                        uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, hipStream_t s)
 {
+    const int64_t tm = (T + 255) / 256;
+    const int64_t big = tm * ((N + 255) / 256), small = tm * ((N + 127) / 128);
+    const double cost_big = (double)((big + kCUs - 1) / kCUs);
+    const double cost_small = 0.5 * 1.1 * (double)((small + kCUs - 1) / kCUs);
+    if (cost_small < cost_big)
+        return launch_cfg<256, 128, 128, 2, 4, 2, 4>(Wq, sW, T, K, N, Y, acc, ws, L, s);
     return launch_cfg<256, 256, 128, 2, 2, 4, 4>(Wq, sW, T, K, N, Y, acc, ws, L, s);
 }
 

@@ -258,6 +258,33 @@ def test_determinism_and_canary():
     assert np.all(host(buf[T * N:]) == sentinel)
 
 
+def test_large_tile_ragged_sampled():
+    """Ragged T and N where the 256x256 tiles fill exactly one round of
+    workgroups (so the library keeps them), checked on sampled rows,
+    accumulators included."""
+    T, K, N = 1000, 272, 16300
+    w = workloads.WORKLOADS["prefill_7b_ffn_up"]
+    X, _ = workloads.make_activation(w, seed=5, T=T, K=K)
+    W = workloads.make_weight(w, seed=6, N=N, K=K)
+    say(f"case large-tile ragged: T={T} K={K} N={N}")
+    Xd, Wd = dev(X), dev(W)
+    Wq, sW = li8.quantize_weight(Wd)
+    ws = li8.new_workspace(T, K, N, DEV)
+    Y = li8.linear(Xd, Wq, sW, 6.0, workspace=ws)
+    li8.prepare(Xd, Wq, 6.0, ws)
+    acc = torch.empty((T, N), dtype=torch.int32, device=DEV)
+    Y2 = li8.gemm(Wq, sW, T, ws, acc=acc)
+    Wq_o, sW_o = oracle.quantize_weight(W)
+    rows = np.array([0, 1, 255, 256, 511, 767, 768, 998, 999])
+    Yo, idx, Xq_o, sX_o, acc_o = oracle.linear_rows(X, Wq_o, sW_o, 6.0, rows)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(host(acc.index_select(0, rows_t)), acc_o)
+    yg = host(Y.index_select(0, rows_t))
+    assert np.array_equal(yg.view(np.uint16), host(Y2.index_select(0, rows_t)).view(np.uint16))
+    e = rel_err(yg, Yo)
+    assert e <= TOL, f"fp16 output error {e}"
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, sampled rows
 # ---------------------------------------------------------------------------
