@@ -175,6 +175,23 @@ def test_decode_many_outliers():
     assert o["nO"] > 150
 
 
+@pytest.mark.parametrize("n_out", [250, 257])
+def test_outlier_count_at_gather_capacity(n_out):
+    """Hundreds of outlier columns on either side of a multiple of 16 (the
+    gathered matrices are padded to one), spread over every 128-column K
+    stage of the GEMM, including the ragged last one (K = 1040 = 8*128 + 16)."""
+    T, K, N = 300, 1040, 520
+    rng = np.random.default_rng(n_out)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    cols = np.sort(rng.choice(K - 16, n_out - 1, replace=False))
+    cols = np.append(cols, K - 7)   # one in the last, partial stage
+    X[:, cols] = rng.choice([-1.0, 1.0], (T, n_out)) * rng.uniform(20, 60, (T, n_out))
+    X = X.astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = check_full(X, W, 6.0, f"{n_out} outlier columns")
+    assert o["nO"] == n_out
+
+
 def test_many_outliers_13b_like():
     """Hundreds of outlier columns (token-sparse outliers as in the 13B
     workload, at a higher rate) on a reduced shape."""
