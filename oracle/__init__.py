@@ -60,8 +60,11 @@ def lib():
         L.oracle_decomposed_output.argtypes = [_u16p, _i32p, _f32p, _i8p, _f32p,
                                                _i32p, ctypes.c_int32,
                                                _i64, _i64, _i64, _u16p]
+        L.oracle_decomposed_output_fp16w.argtypes = [_u16p, _i32p, _f32p, _f32p, _u16p,
+                                                     _i32p, ctypes.c_int32,
+                                                     _i64, _i64, _i64, _u16p]
         L.oracle_linear.restype = ctypes.c_int
-        L.oracle_linear.argtypes = [_u16p, _i8p, _f32p, ctypes.c_double,
+        L.oracle_linear.argtypes = [_u16p, _i8p, _f32p, _u16p, ctypes.c_double,
                                     _i64, _i64, _i64, _u16p,
                                     _u8p, _i32p, _i32p, _i8p, _f32p, _i32p]
         L.oracle_num_threads.restype = ctypes.c_int
@@ -146,8 +149,10 @@ def int8_gemm(Xq, Wq):
     return acc
 
 
-def decomposed_output(X, acc, sX, Wq, sW, idx):
-    """Y fp16 [R,N] from the int8 part (acc, sX, sW) and the outlier columns."""
+def decomposed_output(X, acc, sX, Wq, sW, idx, W16=None):
+    """Y fp16 [R,N] from the int8 part (acc, sX, sW) and the outlier columns;
+    with W16 (the fp16 weight [N,K]) the outlier columns use it instead of
+    the dequantized codes."""
     X = _f16bits(X)
     R, K = X.shape
     N = Wq.shape[0]
@@ -162,15 +167,24 @@ def decomposed_output(X, acc, sX, Wq, sW, idx):
     else:
         nO = len(idx)
     Y = np.empty((R, N), np.uint16)
-    lib().oracle_decomposed_output(_p(X, _u16p), _p(acc, _i32p), _p(sX, _f32p),
-                                   _p(Wq, _i8p), _p(sW, _f32p), _p(idx, _i32p), nO,
-                                   R, K, N, _p(Y, _u16p))
+    if W16 is None:
+        lib().oracle_decomposed_output(_p(X, _u16p), _p(acc, _i32p), _p(sX, _f32p),
+                                       _p(Wq, _i8p), _p(sW, _f32p), _p(idx, _i32p), nO,
+                                       R, K, N, _p(Y, _u16p))
+    else:
+        W16 = _f16bits(W16)
+        lib().oracle_decomposed_output_fp16w(_p(X, _u16p), _p(acc, _i32p), _p(sX, _f32p),
+                                             _p(sW, _f32p), _p(W16, _u16p), _p(idx, _i32p), nO,
+                                             R, K, N, _p(Y, _u16p))
     return Y.view(np.float16)
 
 
-def linear(X, Wq, sW, threshold: float, stages: bool = False):
-    """The whole call.  Returns Y fp16 [T,N], or a dict with every stage."""
+def linear(X, Wq, sW, threshold: float, stages: bool = False, W16=None):
+    """The whole call.  Returns Y fp16 [T,N], or a dict with every stage.
+    With W16 (the fp16 weight) the outlier columns use it (the fp16-weight
+    variant)."""
     X = _f16bits(X)
+    W16 = None if W16 is None else _f16bits(W16)
     T, K = X.shape
     Wq = np.ascontiguousarray(Wq, dtype=np.int8)
     sW = np.ascontiguousarray(sW, dtype=np.float32)
@@ -182,7 +196,8 @@ def linear(X, Wq, sW, threshold: float, stages: bool = False):
     sX = np.empty(max(T, 1), np.float32)
     acc = np.empty((T, N), np.int32)
     nO = ctypes.c_int32(0)
-    rc = lib().oracle_linear(_p(X, _u16p), _p(Wq, _i8p), _p(sW, _f32p), float(threshold),
+    w16p = None if W16 is None else _p(W16, _u16p)
+    rc = lib().oracle_linear(_p(X, _u16p), _p(Wq, _i8p), _p(sW, _f32p), w16p, float(threshold),
                              T, K, N, _p(Y, _u16p), _p(flags, _u8p), ctypes.byref(nO),
                              _p(idx, _i32p), _p(Xq, _i8p), _p(sX, _f32p), _p(acc, _i32p))
     if rc != 0:
@@ -194,7 +209,7 @@ def linear(X, Wq, sW, threshold: float, stages: bool = False):
                 Xq=Xq, sX=sX[:T].copy(), acc=acc)
 
 
-def linear_rows(X, Wq, sW, threshold: float, rows):
+def linear_rows(X, Wq, sW, threshold: float, rows, W16=None):
     """Y for a subset of rows of a (possibly very large) call.
 
     The outlier set depends on every row of X, so detection runs over all
@@ -207,5 +222,5 @@ def linear_rows(X, Wq, sW, threshold: float, rows):
     Xr = np.ascontiguousarray(X[np.asarray(rows)])
     Xq, sX = quantize_rows(Xr, flags)
     acc = int8_gemm(Xq, Wq)
-    Y = decomposed_output(Xr, acc, sX, Wq, sW, idx)
+    Y = decomposed_output(Xr, acc, sX, Wq, sW, idx, W16=W16)
     return Y, idx, Xq, sX, acc

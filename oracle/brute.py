@@ -58,8 +58,10 @@ def quantize_weight(Wbits):
     return Wq, sW
 
 
-def linear(Xbits, Wq, sW, threshold: float):
-    """Returns dict(flags, idx, Xq, sX, acc, Y_bits) for X given as bit rows."""
+def linear(Xbits, Wq, sW, threshold: float, Wbits=None):
+    """Returns dict(flags, idx, Xq, sX, acc, Y_bits) for X given as bit rows.
+    With Wbits (the fp16 weight as bit rows) the outlier columns are
+    multiplied by the fp16 weight instead of the dequantized codes."""
     T = len(Xbits)
     K = len(Xbits[0]) if T else len(Wq[0]) if Wq else 0
     X = [[h2f(b) for b in row] for row in Xbits]
@@ -85,7 +87,7 @@ def linear(Xbits, Wq, sW, threshold: float):
             d = f32(d * sW[n])
             e = 0.0
             for j in idx:
-                w = float(Wq[n][j]) * sW[n]
+                w = h2f(Wbits[n][j]) if Wbits is not None else float(Wq[n][j]) * sW[n]
                 e += X[t][j] * w
             yrow.append(f2h(d + e))
         Y.append(yrow)

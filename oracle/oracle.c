@@ -36,7 +36,8 @@
  *   - The int8 products are summed exactly (int32).  The dequantized value is
  *     fl32(fl32(acc * sX[t]) * sW[n]).
  *   - The weight used for the outlier columns is the dequantized int8 weight
- *     Wq[n,j] * sW[n] (only Wq and sW are kept once the weight is quantized).
+ *     Wq[n,j] * sW[n] (only Wq and sW are kept once the weight is quantized);
+ *     a variant takes the original fp16 weight there instead.
  *     The outlier sum and the final addition are done in fp64 and rounded
  *     once, half-to-even, to fp16.
  *
@@ -234,9 +235,42 @@ void oracle_decomposed_output(const uint16_t *X, const int32_t *acc,
     }
 }
 
+/*
+ * The variant in which the outlier columns are multiplied by the original
+ * fp16 weight rather than by its dequantized codes (hncyxsy.com/news/230290,
+ * section 2.1: the weight sub-matrix of the outlier columns is extracted and
+ * multiplied in fp16 together with the outlier columns of X).  W16 is the
+ * fp16 weight [N,K] that Wq and sW were quantized from.
+ *   D = fl32(fl32(acc * sX[t]) * sW[n])             (int8 part, unchanged)
+ *   E = sum_{j outlier} X[t,j] * W16[n,j]   in fp64 (fp16 part)
+ *   Y = fp16_rne(D + E)
+ */
+void oracle_decomposed_output_fp16w(const uint16_t *X, const int32_t *acc,
+                                    const float *sX, const float *sW, const uint16_t *W16,
+                                    const int32_t *idx, int32_t nO,
+                                    int64_t R, int64_t K, int64_t N, uint16_t *Y)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < R; t++) {
+        for (int64_t n = 0; n < N; n++) {
+            const uint16_t *x = X + t * K;
+            float d = (float)acc[t * N + n] * sX[t];
+            d = d * sW[n];
+            double e = 0.0;
+            for (int32_t i = 0; i < nO; i++) {
+                int64_t j = idx[i];
+                e += oracle_h2d(x[j]) * oracle_h2d(W16[n * K + j]);
+            }
+            Y[t * N + n] = oracle_d2h((double)d + e);
+        }
+    }
+}
+
 /* The whole call: Y[T,N] = decomposed X * W^T, plus optional stage outputs. */
-int oracle_linear(const uint16_t *X, const int8_t *Wq, const float *sW, double thr,
-                  int64_t T, int64_t K, int64_t N, uint16_t *Y,
+/* W16 may be NULL (outliers times the dequantized codes) or the fp16 weight
+   (the fp16-weight variant above). */
+int oracle_linear(const uint16_t *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
+                  double thr, int64_t T, int64_t K, int64_t N, uint16_t *Y,
                   uint8_t *flags_out, int32_t *nO_out, int32_t *idx_out,
                   int8_t *Xq_out, float *sX_out, int32_t *acc_out)
 {
@@ -251,7 +285,10 @@ int oracle_linear(const uint16_t *X, const int8_t *Wq, const float *sW, double t
     oracle_detect_outliers(X, T, K, thr, flags, &nO, idx);
     oracle_quantize_rows(X, T, K, flags, Xq, sX);
     oracle_int8_gemm(Xq, Wq, T, N, K, acc);
-    oracle_decomposed_output(X, acc, sX, Wq, sW, idx, nO, T, K, N, Y);
+    if (W16)
+        oracle_decomposed_output_fp16w(X, acc, sX, sW, W16, idx, nO, T, K, N, Y);
+    else
+        oracle_decomposed_output(X, acc, sX, Wq, sW, idx, nO, T, K, N, Y);
     if (nO_out)
         *nO_out = nO;
     if (!flags_out) free(flags);

@@ -401,3 +401,89 @@ def test_brute_force_on_tiny_workload_rows():
     r = oracle.linear(X, Wq, sW, 6.0, stages=True)
     assert b["idx"] == list(r["idx"]) and len(b["idx"]) >= 1
     assert np.array_equal(r["Y"].view(np.uint16), np.array(b["Y_bits"], np.uint16))
+
+
+# --------------------------------------------------------------------------
+# fp16-weight variant: the outlier columns multiply the original fp16 weight
+# (hncyxsy.com/news/230290, section 2.1: the weight sub-matrix of the outlier
+# columns is extracted and multiplied in fp16)
+# --------------------------------------------------------------------------
+
+def _dyadic(rng, shape):
+    """Values k/64 with |k| <= 256 (exact in fp16): every product is a
+    multiple of 2^-12 below 16 in magnitude, so every fp64 sum of them here
+    is exact whatever the order."""
+    return (rng.integers(-256, 257, shape) / 64.0).astype(np.float16)
+
+
+def test_fp16w_threshold_zero_is_the_rounded_exact_matmul():
+    """At threshold 0 every column with a non-zero value is an outlier, the
+    int8 part is 0, and Y must be the correctly rounded fp16 of X W^T."""
+    rng = np.random.default_rng(3)
+    X = _dyadic(rng, (12, 40))
+    W = _dyadic(rng, (20, 40))
+    X[:, 5] = 0.0   # all zero: not an outlier, and contributes nothing either way
+    Wq, sW = oracle.quantize_weight(W)
+    r = oracle.linear(X, Wq, sW, 0.0, stages=True, W16=W)
+    assert np.all(r["Xq"] == 0) and 5 not in set(r["idx"])
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.array_equal(r["Y"].view(np.uint16), exact.astype(np.float16).view(np.uint16))
+
+
+def test_fp16w_threshold_inf_equals_the_int8_path():
+    X, W, _ = workloads.make("tiny")
+    Wq, sW = oracle.quantize_weight(W)
+    a = oracle.linear(X, Wq, sW, np.inf)
+    b = oracle.linear(X, Wq, sW, np.inf, W16=W)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_fp16w_matches_dequantized_variant_on_grid_weights():
+    """A weight already on its int8 grid with a power-of-two scale
+    (W = q * 2^-e, some |q| = 127 per row) quantizes back to q and 2^-e
+    exactly, so both variants multiply the outliers by the same values."""
+    rng = np.random.default_rng(9)
+    N, K = 24, 48
+    q = rng.integers(-127, 128, (N, K))
+    q[:, 0] = 127
+    e = rng.integers(3, 9, N)
+    W = (q * 2.0 ** -e[:, None]).astype(np.float16)
+    Wq, sW = oracle.quantize_weight(W)
+    assert np.array_equal(Wq, q.astype(np.int8)) and np.array_equal(sW, (2.0 ** -e).astype(np.float32))
+    X, _, _ = workloads.make("tiny", T=10, K=K, N=N)
+    for thr in (6.0, 0.0, 1.0):
+        a = oracle.linear(X, Wq, sW, thr)
+        b = oracle.linear(X, Wq, sW, thr, W16=W)
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), thr
+
+
+def test_fp16w_error_bound_against_exact_matmul():
+    """Only the normal columns carry quantization error now; the outlier
+    columns are exact up to the fp64 sum."""
+    for thr in (6.0, 0.0, np.inf):
+        X, W, _ = workloads.make("tiny")
+        Wq, sW = oracle.quantize_weight(W)
+        r = oracle.linear(X, Wq, sW, thr, stages=True, W16=W)
+        x = X.astype(np.float64)
+        w = W.astype(np.float64)
+        exact = x @ w.T
+        out = r["flags"].astype(bool)
+        sX = r["sX"].astype(np.float64)
+        sWd = sW.astype(np.float64)
+        bound = (np.abs(x[:, ~out]).sum(1)[:, None] * sWd[None, :] / 2
+                 + sX[:, None] * np.abs(w[:, ~out]).sum(1)[None, :] / 2
+                 + (~out).sum() * sX[:, None] * sWd[None, :] / 4)
+        y = r["Y"].astype(np.float64)
+        slack = np.abs(y) * 2.0 ** -10 + 2.0 ** -24 + 1e-6 * bound
+        assert np.all(np.abs(y - exact) <= bound + slack), thr
+
+
+@settings(max_examples=80, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(_case())
+def test_fp16w_brute_force_agrees_bit_exactly(case):
+    X, W, thr = case
+    Wq, sW = oracle.quantize_weight(W)
+    bWq, bsW = brute.quantize_weight(W.view(np.uint16).tolist())
+    r = oracle.linear(X, Wq, sW, thr, W16=W)
+    b = brute.linear(X.view(np.uint16).tolist(), bWq, bsW, thr, Wbits=W.view(np.uint16).tolist())
+    assert np.array_equal(r.view(np.uint16), np.array(b["Y_bits"], np.uint16).reshape(r.shape))
