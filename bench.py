@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--threshold", type=float, default=None)
+    ap.add_argument("--variant", choices=["int8w", "fp16w"], default="int8w",
+                    help="outlier columns times the dequantized codes (default) or the fp16 weight")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables it)")
     ap.add_argument("--no-reference", action="store_true",
@@ -129,8 +131,27 @@ def main():
     Y = torch.empty((T, N), dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
 
+    if args.variant == "fp16w":
+        def call():
+            li8.linear_fp16w(X, Wq, sW, W, thr, out=Y, workspace=ws)
+
+        def prep():
+            li8.prepare_fp16w(X, W, thr, ws)
+
+        def gemm():
+            li8.gemm_fp16w(Wq, sW, W, T, ws, out=Y)
+    else:
+        def call():
+            li8.linear(X, Wq, sW, thr, out=Y, workspace=ws)
+
+        def prep():
+            li8.prepare(X, Wq, thr, ws)
+
+        def gemm():
+            li8.gemm(Wq, sW, T, ws, out=Y)
+
     for _ in range(args.warmup):
-        li8.linear(X, Wq, sW, thr, out=Y, workspace=ws)
+        call()
     torch.cuda.synchronize()
     y_eager = Y.clone()
 
@@ -157,7 +178,7 @@ def main():
     # point, so that the host's per-call launch cost (Python, ctypes) does
     # not pace a short call; the graph's output is checked against the eager
     # call before and after timing.
-    g_lin = capture(lambda: li8.linear(X, Wq, sW, thr, out=Y, workspace=ws), args.steps)
+    g_lin = capture(call, args.steps)
     Y.zero_()
     g_lin.replay()
     torch.cuda.synchronize()
@@ -187,8 +208,8 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / R
 
-    g_prep = capture(lambda: li8.prepare(X, Wq, thr, ws), R)
-    g_gemm = capture(lambda: li8.gemm(Wq, sW, T, ws, out=Y), R)
+    g_prep = capture(prep, R)
+    g_gemm = capture(gemm, R)
     prep_ms = graph_ms(g_prep)
     gemm_ms = graph_ms(g_gemm)
     same_as_eager("prepare + gemm")
@@ -276,7 +297,8 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": w.desc, "name": args.workload, "T": T, "K": K, "N": N,
-                   "threshold": thr, "n_outliers": nO, "parallelism": "single GPU"},
+                   "threshold": thr, "n_outliers": nO, "outlier_weight": args.variant,
+                   "parallelism": "single GPU"},
         "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
         "path": "few-token fused kernel" if few else "prepare kernels + tiled GEMM",
         "prepare_us": round(prep_ms * 1e3, 2),

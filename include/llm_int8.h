@@ -133,6 +133,43 @@ li8_status llm_int8_gemm(const int8_t *Wq, const float *sW,
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The fp16-weight variant (hncyxsy.com/news/230290, section 2.1: the weight
+ * sub-matrix of the outlier columns is extracted and multiplied in fp16 with
+ * the outlier columns of X).  The outlier columns multiply the original
+ * fp16 weight W instead of the dequantized codes Wq*sW:
+ *   Y[t,n] = fp16( fl32(fl32(acc[t,n] * sX[t]) * sW[n]) + sum_{j in O} X[t,j] * W[n,j] )
+ * (the outlier sum accumulated in fp32 on the GPU).  With threshold 0 every
+ * column that has a non-zero value is an outlier and Y is the fp16 product
+ * X . W^T; with threshold +inf it equals llm_int8_linear bit for bit.
+ *   W   [N,K] fp16, read only: the weight that Wq and sW were quantized
+ *       from (16-byte aligned; may be NULL only when T, N or K is 0).
+ * Everything else as for llm_int8_linear; the workspace size is the same.
+ * Equivalent to llm_int8_prepare_fp16w followed by llm_int8_gemm_fp16w.
+ */
+li8_status llm_int8_linear_fp16w(const void *X, const int8_t *Wq, const float *sW,
+                                 const void *W, float threshold, int64_t T, int64_t K,
+                                 int64_t N, void *Y, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * First half of llm_int8_linear_fp16w: as llm_int8_prepare, but the outlier
+ * columns gathered on the weight side are those of the fp16 W.
+ */
+li8_status llm_int8_prepare_fp16w(const void *X, const void *W, float threshold,
+                                  int64_t T, int64_t K, int64_t N,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * Second half of llm_int8_linear_fp16w: as llm_int8_gemm on a workspace
+ * prepared by llm_int8_prepare_fp16w (W is read directly when T <= 16).
+ */
+li8_status llm_int8_gemm_fp16w(const int8_t *Wq, const float *sW, const void *W,
+                               int64_t T, int64_t K, int64_t N, void *Y,
+                               int32_t *acc, const void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Copies the intermediate results of the last llm_int8_prepare on
  * `workspace` into caller buffers (device-to-device, on `stream`).  A test
  * hook: the product path never needs it.  Any output pointer may be NULL.

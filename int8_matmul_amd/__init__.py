@@ -29,7 +29,8 @@ import torch
 __all__ = [
     "Int8MatmulError", "LibraryNotBuilt", "library_path", "load_library",
     "quantize_weight", "workspace_bytes", "new_workspace", "linear", "prepare",
-    "gemm", "export_stages", "few_token_path", "STATUS",
+    "gemm", "export_stages", "few_token_path", "linear_fp16w", "prepare_fp16w",
+    "gemm_fp16w", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +96,13 @@ def load_library() -> ctypes.CDLL:
     L.llm_int8_prepare.argtypes = [vp, vp, ctypes.c_float, i64, i64, i64, vp, sz, vp]
     L.llm_int8_gemm.restype = ctypes.c_int
     L.llm_int8_gemm.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    L.llm_int8_linear_fp16w.restype = ctypes.c_int
+    L.llm_int8_linear_fp16w.argtypes = [vp, vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp,
+                                        sz, vp]
+    L.llm_int8_prepare_fp16w.restype = ctypes.c_int
+    L.llm_int8_prepare_fp16w.argtypes = [vp, vp, ctypes.c_float, i64, i64, i64, vp, sz, vp]
+    L.llm_int8_gemm_fp16w.restype = ctypes.c_int
+    L.llm_int8_gemm_fp16w.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
     L.llm_int8_export_stages.restype = ctypes.c_int
     L.llm_int8_export_stages.argtypes = [vp, sz, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
     _lib = L
@@ -211,6 +219,66 @@ def gemm(Wq: torch.Tensor, sW: torch.Tensor, T: int, workspace: torch.Tensor,
     _check("llm_int8_gemm",
            L.llm_int8_gemm(_ptr(Wq), _ptr(sW), T, K, N, _ptr(out), _ptr(acc), _ptr(workspace),
                            workspace.numel(), _stream(Wq.device)))
+    return out
+
+
+def linear_fp16w(X: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, W: torch.Tensor,
+                 threshold: float = 6.0, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None):
+    """The fp16-weight variant: the outlier columns multiply the fp16 weight
+    W [N,K] (the one Wq, sW were quantized from) instead of Wq*sW."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(sW, torch.float32, "sW", 1)
+    _require(W, torch.float16, "W", 2)
+    T, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or sW.shape[0] != N or tuple(W.shape) != (N, K):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, "
+                         f"sW {tuple(sW.shape)}, W {tuple(W.shape)}")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    _require(out, torch.float16, "out", 2)
+    ws = _ws(workspace, T, K, N, X.device)
+    _check("llm_int8_linear_fp16w",
+           L.llm_int8_linear_fp16w(_ptr(X), _ptr(Wq), _ptr(sW), _ptr(W), float(threshold), T, K,
+                                   N, _ptr(out), _ptr(ws), ws.numel(), _stream(X.device)))
+    return out
+
+
+def prepare_fp16w(X: torch.Tensor, W: torch.Tensor, threshold: float, workspace: torch.Tensor):
+    """`prepare` of the fp16-weight variant (gathers the outlier columns of W)."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(W, torch.float16, "W", 2)
+    T, K = X.shape
+    N = W.shape[0]
+    ws = _ws(workspace, T, K, N, X.device)
+    _check("llm_int8_prepare_fp16w",
+           L.llm_int8_prepare_fp16w(_ptr(X), _ptr(W), float(threshold), T, K, N, _ptr(ws),
+                                    ws.numel(), _stream(X.device)))
+    return ws
+
+
+def gemm_fp16w(Wq: torch.Tensor, sW: torch.Tensor, W: torch.Tensor, T: int,
+               workspace: torch.Tensor, out: torch.Tensor | None = None,
+               acc: torch.Tensor | None = None):
+    """`gemm` of the fp16-weight variant, on a workspace from `prepare_fp16w`."""
+    L = load_library()
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(sW, torch.float32, "sW", 1)
+    _require(W, torch.float16, "W", 2)
+    N, K = Wq.shape
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=Wq.device)
+    _require(out, torch.float16, "out", 2)
+    if acc is not None:
+        _require(acc, torch.int32, "acc", 2)
+    _require(workspace, torch.uint8, "workspace", 1)
+    _check("llm_int8_gemm_fp16w",
+           L.llm_int8_gemm_fp16w(_ptr(Wq), _ptr(sW), _ptr(W), T, K, N, _ptr(out), _ptr(acc),
+                                 _ptr(workspace), workspace.numel(), _stream(Wq.device)))
     return out
 
 

@@ -97,6 +97,39 @@ li8_status check_gemm_args(const int8_t *Wq, const float *sW, int64_t T, int64_t
     return LI8_OK;
 }
 
+// W16 null: the int8 path; else the fp16-weight variant.
+li8_status gemm_common(const int8_t *Wq, const float *sW, const uint16_t *W16, int64_t T,
+                       int64_t K, int64_t N, void *Y, int32_t *acc, const void *workspace,
+                       hipStream_t stream)
+{
+    const WsLayout L = ws_layout(T, K, N);
+    if (decode_shape(T, K))
+        return from_hip(launch_decode_gemm(Wq, sW, W16, T, K, N, static_cast<uint16_t *>(Y), acc,
+                                           static_cast<const char *>(workspace), L, stream));
+    return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), acc,
+                                static_cast<const char *>(workspace), L, W16 != nullptr, stream));
+}
+
+// W16 null: the int8 path; else the fp16-weight variant.
+li8_status linear_common(const void *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
+                         float threshold, int64_t T, int64_t K, int64_t N, void *Y,
+                         void *workspace, hipStream_t stream)
+{
+    // few tokens: one kernel, bit-identical to the prepare + gemm pair
+    if (decode_shape(T, K))
+        return from_hip(launch_decode_fused(static_cast<const uint16_t *>(X), Wq, sW, W16,
+                                            threshold_magnitude(threshold), T, K, N,
+                                            static_cast<uint16_t *>(Y), stream));
+    const WsLayout L = ws_layout(T, K, N);
+    hipError_t e = launch_prepare(static_cast<const uint16_t *>(X), Wq, W16,
+                                  threshold_magnitude(threshold), T, K, N,
+                                  static_cast<char *>(workspace), L, stream);
+    if (e != hipSuccess)
+        return LI8_ERR_HIP;
+    return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), nullptr,
+                                static_cast<const char *>(workspace), L, W16 != nullptr, stream));
+}
+
 } // namespace
 
 extern "C" {
@@ -145,9 +178,23 @@ li8_status llm_int8_prepare(const void *X, const int8_t *Wq, float threshold, in
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     const WsLayout L = ws_layout(T, K, N);
-    return from_hip(launch_prepare(static_cast<const uint16_t *>(X), Wq,
+    return from_hip(launch_prepare(static_cast<const uint16_t *>(X), Wq, nullptr,
                                    threshold_magnitude(threshold), T, K, N,
                                    static_cast<char *>(workspace), L, stream));
+}
+
+li8_status llm_int8_prepare_fp16w(const void *X, const void *W, float threshold, int64_t T,
+                                  int64_t K, int64_t N, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream)
+{
+    li8_status st = check_linear_args(X, static_cast<const int8_t *>(W), threshold, T, K, N,
+                                      workspace, workspace_bytes);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    const WsLayout L = ws_layout(T, K, N);
+    return from_hip(launch_prepare(static_cast<const uint16_t *>(X), nullptr,
+                                   static_cast<const uint16_t *>(W), threshold_magnitude(threshold),
+                                   T, K, N, static_cast<char *>(workspace), L, stream));
 }
 
 li8_status llm_int8_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
@@ -157,12 +204,24 @@ li8_status llm_int8_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K
     li8_status st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
-    const WsLayout L = ws_layout(T, K, N);
-    if (decode_shape(T, K))
-        return from_hip(launch_decode_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), acc,
-                                           static_cast<const char *>(workspace), L, stream));
-    return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), acc,
-                                static_cast<const char *>(workspace), L, stream));
+    return gemm_common(Wq, sW, nullptr, T, K, N, Y, acc, workspace, stream);
+}
+
+li8_status llm_int8_gemm_fp16w(const int8_t *Wq, const float *sW, const void *W, int64_t T,
+                               int64_t K, int64_t N, void *Y, int32_t *acc, const void *workspace,
+                               size_t workspace_bytes, hipStream_t stream)
+{
+    li8_status st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes);
+    if (st == LI8_OK && T > 0 && N > 0 && K > 0) {
+        if (!W)
+            st = LI8_ERR_INVALID_ARG;
+        else if (misaligned(W))
+            st = LI8_ERR_ALIGN;
+    }
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    return gemm_common(Wq, sW, static_cast<const uint16_t *>(W), T, K, N, Y, acc, workspace,
+                       stream);
 }
 
 li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW, float threshold,
@@ -174,19 +233,26 @@ li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW, flo
         st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
-    // few tokens: one kernel, bit-identical to the prepare + gemm pair
-    if (decode_shape(T, K))
-        return from_hip(launch_decode_fused(static_cast<const uint16_t *>(X), Wq, sW,
-                                            threshold_magnitude(threshold), T, K, N,
-                                            static_cast<uint16_t *>(Y), stream));
-    const WsLayout L = ws_layout(T, K, N);
-    hipError_t e = launch_prepare(static_cast<const uint16_t *>(X), Wq,
-                                  threshold_magnitude(threshold), T, K, N,
-                                  static_cast<char *>(workspace), L, stream);
-    if (e != hipSuccess)
-        return LI8_ERR_HIP;
-    return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), nullptr,
-                                static_cast<const char *>(workspace), L, stream));
+    return linear_common(X, Wq, sW, nullptr, threshold, T, K, N, Y, workspace, stream);
+}
+
+li8_status llm_int8_linear_fp16w(const void *X, const int8_t *Wq, const float *sW, const void *W,
+                                 float threshold, int64_t T, int64_t K, int64_t N, void *Y,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    if (st == LI8_OK)
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
+    if (st == LI8_OK && T > 0 && N > 0 && K > 0) {
+        if (!W)
+            st = LI8_ERR_INVALID_ARG;
+        else if (misaligned(W))
+            st = LI8_ERR_ALIGN;
+    }
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    return linear_common(X, Wq, sW, static_cast<const uint16_t *>(W), threshold, T, K, N, Y,
+                         workspace, stream);
 }
 
 li8_status llm_int8_export_stages(const void *workspace, size_t workspace_bytes, int64_t T,

@@ -30,7 +30,9 @@
 // The variant FUSED = false reads the token codes, scales and outlier
 // columns that the prepare kernels left in the workspace instead of
 // deriving them; everything after that is the same code, so the two
-// variants give bit-identical results.
+// variants give bit-identical results.  F16W: the outlier columns multiply
+// the original fp16 weight W16 (the fp16-weight variant), and the sum is
+// D = fl32(fl32(acc * sX) * sW) + sum_O X * W16.
 #include "li8_internal.h"
 #include "quant_math.h"
 
@@ -108,9 +110,10 @@ __device__ void outlier_columns8(const uint32_t *bits, const int32_t *pre, int n
     }
 }
 
-template <bool FUSED, int KB, bool STORE_ACC>
+template <bool FUSED, int KB, bool F16W, bool STORE_ACC>
 __global__ __launch_bounds__(kDThreads) void k_decode(
     const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq, const float *__restrict__ sW,
+    const uint16_t *__restrict__ W16,
     uint32_t thr_mag, int T, int K, int N,
     const int32_t *__restrict__ meta, const int32_t *__restrict__ idx_g,
     const float *__restrict__ sX_g, const int8_t *__restrict__ Xq_g,
@@ -335,7 +338,10 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         const int64_t trow = (int64_t)min(tok, T - 1) * K;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            wr[e] = Wq[(int64_t)wrow * K + col[e]];
+            if constexpr (F16W)
+                wr[e] = W16[(int64_t)wrow * K + col[e]];
+            else
+                wr[e] = Wq[(int64_t)wrow * K + col[e]];
             xr[e] = FUSED ? X[trow + col[e]] : XO_g[trow + ((i0 + e < nO) ? i0 + e : 0)];
         }
     };
@@ -343,7 +349,10 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             const bool ok = i0 + e < nO;
-            a[e] = ok ? (_Float16)(float)wr[e] : (_Float16)0.0f;
+            if constexpr (F16W)
+                a[e] = ok ? __builtin_bit_cast(_Float16, (uint16_t)wr[e]) : (_Float16)0.0f;
+            else
+                a[e] = ok ? (_Float16)(float)wr[e] : (_Float16)0.0f;
             b[e] = (ok && tok < T) ? __builtin_bit_cast(_Float16, (uint16_t)xr[e]) : (_Float16)0.0f;
         }
     };
@@ -394,6 +403,10 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
 #pragma unroll
         for (int r = 0; r < 4; r++)
             d[r] = (float)tot[r] * sx;
+        if constexpr (F16W)   // the fp16 outlier product is then in output units
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                d[r] *= swv[r];
         // D += X[:, O] . Wq[:, O]^T, 32 outlier columns per MFMA: lane
         // supplies weight row (lane & 15) and token tok at ranks
         // 32c + 8*kg .. +7
@@ -417,7 +430,9 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         for (int r = 0; r < 4; r++) {
             // fl32(D * sW) first, then one rounding to fp16 (the empty asm
             // keeps the product and the conversion from being fused)
-            float p = d[r] * swv[r];
+            float p = d[r];
+            if constexpr (!F16W)
+                p *= swv[r];
             asm("" : "+v"(p));
             h[r] = __builtin_bit_cast(uint16_t, (_Float16)p);
         }
@@ -450,8 +465,9 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     }
 }
 
-template <bool FUSED, int KB>
-hipError_t launch_kb(const uint16_t *X, const int8_t *Wq, const float *sW, uint32_t thr_mag,
+template <bool FUSED, int KB, bool F16W>
+hipError_t launch_kb(const uint16_t *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
+                     uint32_t thr_mag,
                      int64_t T, int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
                      const WsLayout &L, hipStream_t s)
 {
@@ -463,11 +479,11 @@ hipError_t launch_kb(const uint16_t *X, const int8_t *Wq, const float *sW, uint3
     const int8_t *Xq = FUSED ? nullptr : reinterpret_cast<const int8_t *>(ws + L.Xq);
     const uint16_t *XO = FUSED ? nullptr : reinterpret_cast<const uint16_t *>(ws + L.XO);
     if (acc)
-        hipLaunchKernelGGL((k_decode<FUSED, KB, true>), grid, dim3(kDThreads), 0, s, X, Wq, sW,
-                           thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
+        hipLaunchKernelGGL((k_decode<FUSED, KB, F16W, true>), grid, dim3(kDThreads), 0, s, X, Wq,
+                           sW, W16, thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
     else
-        hipLaunchKernelGGL((k_decode<FUSED, KB, false>), grid, dim3(kDThreads), 0, s, X, Wq, sW,
-                           thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
+        hipLaunchKernelGGL((k_decode<FUSED, KB, F16W, false>), grid, dim3(kDThreads), 0, s, X, Wq,
+                           sW, W16, thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
     return hipGetLastError();
 }
 
@@ -479,22 +495,28 @@ bool decode_shape(int64_t T, int64_t K)
 }
 
 hipError_t launch_decode_fused(const uint16_t *X, const int8_t *Wq, const float *sW,
-                               uint16_t thr_mag, int64_t T, int64_t K, int64_t N, uint16_t *Y,
-                               hipStream_t s)
+                               const uint16_t *W16, uint16_t thr_mag, int64_t T, int64_t K,
+                               int64_t N, uint16_t *Y, hipStream_t s)
 {
     static const WsLayout none{};
-    if (K <= 4096)
-        return launch_kb<true, 8>(X, Wq, sW, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
-    return launch_kb<true, 16>(X, Wq, sW, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
+    if (W16)
+        return K <= 4096
+                   ? launch_kb<true, 8, true>(X, Wq, sW, W16, thr_mag, T, K, N, Y, nullptr, nullptr, none, s)
+                   : launch_kb<true, 16, true>(X, Wq, sW, W16, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
+    return K <= 4096
+               ? launch_kb<true, 8, false>(X, Wq, sW, nullptr, thr_mag, T, K, N, Y, nullptr, nullptr, none, s)
+               : launch_kb<true, 16, false>(X, Wq, sW, nullptr, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
 }
 
-hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
-                              uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L,
-                              hipStream_t s)
+hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, const uint16_t *W16, int64_t T,
+                              int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
+                              const WsLayout &L, hipStream_t s)
 {
-    if (K <= 4096)
-        return launch_kb<false, 8>(nullptr, Wq, sW, 0, T, K, N, Y, acc, ws, L, s);
-    return launch_kb<false, 16>(nullptr, Wq, sW, 0, T, K, N, Y, acc, ws, L, s);
+    if (W16)
+        return K <= 4096 ? launch_kb<false, 8, true>(nullptr, Wq, sW, W16, 0, T, K, N, Y, acc, ws, L, s)
+                         : launch_kb<false, 16, true>(nullptr, Wq, sW, W16, 0, T, K, N, Y, acc, ws, L, s);
+    return K <= 4096 ? launch_kb<false, 8, false>(nullptr, Wq, sW, nullptr, 0, T, K, N, Y, acc, ws, L, s)
+                     : launch_kb<false, 16, false>(nullptr, Wq, sW, nullptr, 0, T, K, N, Y, acc, ws, L, s);
 }
 
 } // namespace li8

@@ -84,7 +84,7 @@ __device__ __forceinline__ void wait_loads_barrier()
 
 constexpr int kOutOfRange = (int)0x80000000;   // buffer offset past any operand
 
-template <int BM, int BN, int BKS, int NS, int WM, int WN, int GM, bool STORE_ACC>
+template <int BM, int BN, int BKS, int NS, int WM, int WN, int GM, bool F16W, bool STORE_ACC>
 __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     const int8_t *__restrict__ Xq, const int8_t *__restrict__ Wq,
     const float *__restrict__ sX, const float *__restrict__ sW,
@@ -285,28 +285,62 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     // in the scalar operand
     const int nch = (nO + 15) >> 4;
     const __amdgpu_buffer_rsrc_t rXO = make_rsrc(XO, (int)(2u * (unsigned)T * (unsigned)K));
-    const __amdgpu_buffer_rsrc_t rWO = make_rsrc(WO, N * K);
+    // WO: int8 codes [N,K], or in the fp16-weight variant fp16 [N,K]
+    constexpr int WOE = F16W ? 2 : 1;   // bytes per element
+    const __amdgpu_buffer_rsrc_t rWO = make_rsrc(WO, (int)((unsigned)WOE * (unsigned)N * (unsigned)K));
     int voX[FM], voW[FN];
 #pragma unroll
     for (int a = 0; a < FM; a++)
         voX[a] = (int)((unsigned)min(tok0 + 32 * a, T - 1) * (unsigned)K * 2u + khalf * 16u);
 #pragma unroll
     for (int b = 0; b < FN; b++)
-        voW[b] = min(n0 + wn * FN * 32 + 32 * b + (lane & 31), N - 1) * K + khalf * 8;
+        voW[b] = (int)((unsigned)min(n0 + wn * FN * 32 + 32 * b + (lane & 31), N - 1) * (unsigned)K *
+                           WOE + khalf * 8 * WOE);
     v8h ox[2][FM];
-    v2u ow[2][FN];
+    v2u ow[2][FN];     // int8 codes
+    v8h ow16[2][FN];   // fp16 weight (the fp16-weight variant)
     auto oload = [&](int set, int c) {
 #pragma unroll
         for (int a = 0; a < FM; a++)
             ox[set][a] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rXO, voX[a], c * 32, 0));
+        if constexpr (F16W) {
 #pragma unroll
-        for (int b = 0; b < FN; b++)
-            ow[set][b] = __builtin_amdgcn_raw_buffer_load_b64(rWO, voW[b], c * 16, 0);
+            for (int b = 0; b < FN; b++)
+                ow16[set][b] =
+                    __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rWO, voW[b], c * 32, 0));
+        } else {
+#pragma unroll
+            for (int b = 0; b < FN; b++)
+                ow[set][b] = __builtin_amdgcn_raw_buffer_load_b64(rWO, voW[b], c * 16, 0);
+        }
     };
     if (nch > 0)
         oload(0, 0);
 
-    // D = fl32(acc * sX)
+    // feature scales, four consecutive per float4
+    float4 sw[FN][4];
+    auto load_sw = [&]() {
+        if ((N & 3) == 0) {   // 16-byte loads; a group starting below N ends below N
+#pragma unroll
+            for (int b = 0; b < FN; b++)
+#pragma unroll
+                for (int g = 0; g < 4; g++)
+                    sw[b][g] = *reinterpret_cast<const float4 *>(sW + min(fea0 + 32 * b + 8 * g, N - 4));
+        } else {
+#pragma unroll
+            for (int b = 0; b < FN; b++)
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int n = fea0 + 32 * b + 8 * g;
+                    sw[b][g].x = sW[min(n, N - 1)];
+                    sw[b][g].y = sW[min(n + 1, N - 1)];
+                    sw[b][g].z = sW[min(n + 2, N - 1)];
+                    sw[b][g].w = sW[min(n + 3, N - 1)];
+                }
+        }
+    };
+    // D = fl32(acc * sX); in the fp16-weight variant D = fl32(D * sW) here,
+    // before the outlier product (which is then in output units)
     v16f d[FM][FN];
 #pragma unroll
     for (int a = 0; a < FM; a++)
@@ -315,6 +349,20 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
 #pragma unroll
             for (int r = 0; r < 16; r++)
                 d[a][b][r] = (float)acc[a][b][r] * sx[a];
+    if constexpr (F16W) {
+        load_sw();
+#pragma unroll
+        for (int a = 0; a < FM; a++)
+#pragma unroll
+            for (int b = 0; b < FN; b++)
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    d[a][b][4 * g] *= sw[b][g].x;
+                    d[a][b][4 * g + 1] *= sw[b][g].y;
+                    d[a][b][4 * g + 2] *= sw[b][g].z;
+                    d[a][b][4 * g + 3] *= sw[b][g].w;
+                }
+    }
     // D += XO . WO^T over the outlier columns (codes are exact in fp16),
     // the next chunk's loads in flight during this chunk's MFMAs
     // `keep` is all ones, or zero for a chunk past the end (its codes are
@@ -324,10 +372,16 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
         v8h wb[FN];
 #pragma unroll
         for (int b = 0; b < FN; b++) {
-            const uint32_t w[2] = {ow[set][b][0] & keep, ow[set][b][1] & keep};
+            if constexpr (F16W) {
+                v4i w = __builtin_bit_cast(v4i, ow16[set][b]);
+                w &= (int)keep;
+                wb[b] = __builtin_bit_cast(v8h, w);
+            } else {
+                const uint32_t w[2] = {ow[set][b][0] & keep, ow[set][b][1] & keep};
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-                wb[b][e] = (_Float16)(float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
+                for (int e = 0; e < 8; e++)
+                    wb[b][e] = (_Float16)(float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
+            }
         }
 #pragma unroll
         for (int a = 0; a < FM; a++)
@@ -350,25 +404,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    float4 sw[FN][4];
-    if ((N & 3) == 0) {   // 16-byte loads; a group starting below N ends below N
-#pragma unroll
-        for (int b = 0; b < FN; b++)
-#pragma unroll
-            for (int g = 0; g < 4; g++)
-                sw[b][g] = *reinterpret_cast<const float4 *>(sW + min(fea0 + 32 * b + 8 * g, N - 4));
-    } else {
-#pragma unroll
-        for (int b = 0; b < FN; b++)
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int n = fea0 + 32 * b + 8 * g;
-                sw[b][g].x = sW[min(n, N - 1)];
-                sw[b][g].y = sW[min(n + 1, N - 1)];
-                sw[b][g].z = sW[min(n + 2, N - 1)];
-                sw[b][g].w = sW[min(n + 3, N - 1)];
-            }
-    }
+    if constexpr (!F16W)
+        load_sw();
     // Y = fp16(fl32(D * sW)), four consecutive features per 8-byte LDS write
     // into the wave's staging rows (one row per token).  The ring buffers
     // are reused for the staging: every wave must be done reading them.
@@ -388,7 +425,9 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                     // empty asm keeps the compiler from fusing the product
                     // and the conversion into a single-rounding
                     // v_fma_mixlo_f16
-                    float p = d[a][b][4 * g + j] * s4[j];
+                    float p = d[a][b][4 * g + j];
+                    if constexpr (!F16W)
+                        p *= s4[j];
                     asm("" : "+v"(p));
                     h[j] = __builtin_bit_cast(uint16_t, (_Float16)p);
                 }
@@ -422,7 +461,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     }
 }
 
-template <int BM, int BN, int BKS, int NS, int WM, int WN, int GM>
+template <int BM, int BN, int BKS, int NS, int WM, int WN, int GM, bool F16W>
 hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
                       uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, hipStream_t s)
 {
@@ -436,10 +475,10 @@ hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, i
     const uint16_t *XO = reinterpret_cast<const uint16_t *>(ws + L.XO);
     const int8_t *WO = reinterpret_cast<const int8_t *>(ws + L.WO);
     if (acc)
-        hipLaunchKernelGGL((k_gemm<BM, BN, BKS, NS, WM, WN, GM, true>), grid, block, 0, s, Xq, Wq,
+        hipLaunchKernelGGL((k_gemm<BM, BN, BKS, NS, WM, WN, GM, F16W, true>), grid, block, 0, s, Xq, Wq,
                            sX, sW, meta, XO, WO, (int)T, (int)K, (int)N, tiles_m, tiles_n, Y, acc);
     else
-        hipLaunchKernelGGL((k_gemm<BM, BN, BKS, NS, WM, WN, GM, false>), grid, block, 0, s, Xq, Wq,
+        hipLaunchKernelGGL((k_gemm<BM, BN, BKS, NS, WM, WN, GM, F16W, false>), grid, block, 0, s, Xq, Wq,
                            sX, sW, meta, XO, WO, (int)T, (int)K, (int)N, tiles_m, tiles_n, Y, acc);
     return hipGetLastError();
 }
@@ -455,15 +494,18 @@ hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, i
 constexpr int kCUs = 256;
 
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
-                       uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, hipStream_t s)
+                       uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, bool fp16w,
+                       hipStream_t s)
 {
     const int64_t tm = (T + 255) / 256;
     const int64_t big = tm * ((N + 255) / 256), small = tm * ((N + 127) / 128);
     const double cost_big = (double)((big + kCUs - 1) / kCUs);
     const double cost_small = 0.5 * 1.1 * (double)((small + kCUs - 1) / kCUs);
     if (cost_small < cost_big)
-        return launch_cfg<256, 128, 128, 2, 4, 2, 4>(Wq, sW, T, K, N, Y, acc, ws, L, s);
-    return launch_cfg<256, 256, 128, 2, 2, 4, 4>(Wq, sW, T, K, N, Y, acc, ws, L, s);
+        return fp16w ? launch_cfg<256, 128, 128, 2, 4, 2, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s)
+                     : launch_cfg<256, 128, 128, 2, 4, 2, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s);
+    return fp16w ? launch_cfg<256, 256, 128, 2, 2, 4, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s)
+                 : launch_cfg<256, 256, 128, 2, 2, 4, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s);
 }
 
 } // namespace li8

@@ -32,7 +32,9 @@ constexpr int kDecodeMaxBlocks = 256;   // one workgroup per CU
 //   XO   : fp16[T,K]           X[t, idx[i]] at column i < nO, zero pad to a
 //                              multiple of 16; row stride K
 //   WO   : int8[N,K]           Wq[n, idx[i]] at column i < nO, zero pad to a
-//                              multiple of 16; row stride K
+//                              multiple of 16; row stride K.  In the fp16-weight
+//                              variant the same region holds fp16[N,K] with
+//                              W[n, idx[i]] (hence 2*N*K bytes)
 struct WsLayout {
     size_t bits, meta, idx, sX, Xq, XO, WO, total;
 };
@@ -49,7 +51,7 @@ inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
     L.sX = off;   off = align_up(off + 4 * (size_t)(T ? T : 1), A);
     L.Xq = off;   off = align_up(off + (size_t)T * (size_t)K + 16, A);
     L.XO = off;   off = align_up(off + 2 * (size_t)T * (size_t)K + 16, A);
-    L.WO = off;   off = align_up(off + (size_t)N * (size_t)K + 16, A);
+    L.WO = off;   off = align_up(off + 2 * (size_t)N * (size_t)K + 16, A);
     L.total = off;
     return L;
 }
@@ -57,24 +59,29 @@ inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
 // Launchers (quant.hip).  All asynchronous on `s`; return hipGetLastError().
 hipError_t launch_quantize_weight(const uint16_t *W, int64_t N, int64_t K,
                                   int8_t *Wq, float *sW, hipStream_t s);
-hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, uint16_t thr_mag,
-                          int64_t T, int64_t K, int64_t N, char *ws,
+// W16: null, or the fp16 weight [N,K] whose outlier columns are gathered
+// instead of those of Wq (the fp16-weight variant).
+hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W16,
+                          uint16_t thr_mag, int64_t T, int64_t K, int64_t N, char *ws,
                           const WsLayout &L, hipStream_t s);
 
 // Launcher (gemm.hip).
+// fp16w: the outlier product uses the fp16 weight columns that the prepare
+// call gathered from W16 (and the result is added after the scale sW).
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K,
                        int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
-                       const WsLayout &L, hipStream_t s);
+                       const WsLayout &L, bool fp16w, hipStream_t s);
 
 // Few-token path (decode.hip).  decode_shape(T, K) says whether both
 // entry points use it for this shape; the fused launch does the whole
 // layer from X, the other reads what launch_prepare left in the workspace.
 bool decode_shape(int64_t T, int64_t K);
+// W16 non-null selects the fp16-weight variant.
 hipError_t launch_decode_fused(const uint16_t *X, const int8_t *Wq, const float *sW,
-                               uint16_t thr_mag, int64_t T, int64_t K, int64_t N, uint16_t *Y,
-                               hipStream_t s);
-hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
-                              uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L,
-                              hipStream_t s);
+                               const uint16_t *W16, uint16_t thr_mag, int64_t T, int64_t K,
+                               int64_t N, uint16_t *Y, hipStream_t s);
+hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, const uint16_t *W16, int64_t T,
+                              int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
+                              const WsLayout &L, hipStream_t s);
 
 } // namespace li8

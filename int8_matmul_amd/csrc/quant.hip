@@ -188,13 +188,15 @@ __device__ int load_bits_and_scan(const uint32_t *__restrict__ bits_g, int nw,
 // ---------------------------------------------------------------------------
 // Token quantization + outlier gathers.  Blocks [0, xblocks) each quantize
 // kPrepRows token rows; the remaining blocks gather the outlier columns of
-// wrows rows of Wq each.  Every block rebuilds the prefix counts of the bit
-// set in LDS, which gives each outlier column its compact index.
+// wrows rows of Wq (or of the fp16 weight W16, in the fp16-weight variant)
+// each.  Every block rebuilds the prefix counts of the bit set in LDS, which
+// gives each outlier column its compact index.
 // ---------------------------------------------------------------------------
 
 template <int ROWS>
 __global__ __launch_bounds__(kThreads) void k_prepare(
-    const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq, int T, int K, int N,
+    const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq,
+    const uint16_t *__restrict__ W16, int T, int K, int N,
     int wrows, const uint32_t *__restrict__ bits_g, int32_t *__restrict__ meta,
     int32_t *__restrict__ idx_g, float *__restrict__ sX, int8_t *__restrict__ Xq,
     uint16_t *__restrict__ XO, int8_t *__restrict__ WO)
@@ -342,6 +344,39 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
     __syncthreads();
     const int nnz = nnz_s;
     const int pairs = (n1 - n0) * nnz;
+    if (W16) {   // fp16-weight variant: the outlier columns of W, as fp16
+        uint16_t *WO16 = reinterpret_cast<uint16_t *>(WO);
+        for (int p = tid; p < pairs; p += kThreads) {
+            const int n = n0 + p / nnz;
+            const int w = nzw[p - (p / nnz) * nnz];
+            uint32_t b = bits[w];
+            const uint16_t *src = W16 + (int64_t)n * K + 32 * w;
+            uint32_t hw[16];   // the word's 32 columns, two per register
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (32 * w + 8 * q < K)
+                    v = *reinterpret_cast<const uint4 *>(src + 8 * q);
+                hw[4 * q] = v.x;
+                hw[4 * q + 1] = v.y;
+                hw[4 * q + 2] = v.z;
+                hw[4 * q + 3] = v.w;
+            }
+            uint16_t *dst = WO16 + (int64_t)n * K;
+            int i = pre[w];
+            while (b) {
+                const int j = __ffs(b) - 1;
+                dst[i++] = (uint16_t)((hw[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                b &= b - 1u;
+            }
+        }
+        for (int p = tid; p < (n1 - n0) * 16; p += kThreads) {
+            const int n = n0 + p / 16, e = p % 16;
+            if (nO + e < nO16)
+                WO16[(int64_t)n * K + nO + e] = 0;
+        }
+        return;
+    }
     for (int p = tid; p < pairs; p += kThreads) {
         const int n = n0 + p / nnz;
         const int w = nzw[p - (p / nnz) * nnz];
@@ -377,8 +412,9 @@ hipError_t launch_quantize_weight(const uint16_t *W, int64_t N, int64_t K, int8_
     return hipGetLastError();
 }
 
-hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, uint16_t thr_mag, int64_t T,
-                          int64_t K, int64_t N, char *ws, const WsLayout &L, hipStream_t s)
+hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W16,
+                          uint16_t thr_mag, int64_t T, int64_t K, int64_t N, char *ws,
+                          const WsLayout &L, hipStream_t s)
 {
     uint32_t *bits = reinterpret_cast<uint32_t *>(ws + L.bits);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + L.meta);
@@ -404,7 +440,7 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, uint16_t thr_mag,
     const size_t lds = 12 * (size_t)(nw > 0 ? nw : 1);   // bits, prefix, non-zero words
     const int64_t xblocks = (T + kPrepRows - 1) / kPrepRows;
     hipLaunchKernelGGL(k_prepare<kPrepRows>, dim3((unsigned)(xblocks + wblocks)), dim3(kThreads), lds, s, X, Wq,
-                       (int)T, (int)K, (int)N, wrows, bits, meta,
+                       W16, (int)T, (int)K, (int)N, wrows, bits, meta,
                        reinterpret_cast<int32_t *>(ws + L.idx),
                        reinterpret_cast<float *>(ws + L.sX),
                        reinterpret_cast<int8_t *>(ws + L.Xq),

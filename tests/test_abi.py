@@ -41,6 +41,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "li8_status_str", "int8_quantize_weight", "llm_int8_workspace_bytes",
         "llm_int8_linear", "llm_int8_prepare", "llm_int8_gemm", "llm_int8_export_stages",
+        "llm_int8_linear_fp16w", "llm_int8_prepare_fp16w", "llm_int8_gemm_fp16w",
     ])
 
 
@@ -66,10 +67,11 @@ def test_workspace_bytes(lib):
     assert ws(16, 133152, 16) == 0      # K above the int32 bound
     assert ws(16, 133136, 16) > 0
     a = ws(4096, 4096, 11008)
-    # covers Xq (T*K), the gathered outlier columns of X (2*T*K) and of Wq
-    # (N*K) in the worst case nO = K, plus small tables
-    assert a >= 4096 * 4096 * 3 + 11008 * 4096
-    assert a < 4096 * 4096 * 3 + 11008 * 4096 + (1 << 20)
+    # covers Xq (T*K), the gathered outlier columns of X (2*T*K) and of the
+    # weight (2*N*K: fp16 in the fp16-weight variant) in the worst case
+    # nO = K, plus small tables
+    assert a >= 4096 * 4096 * 3 + 2 * 11008 * 4096
+    assert a < 4096 * 4096 * 3 + 2 * 11008 * 4096 + (1 << 20)
     assert ws(0, 16, 16) > 0 and ws(16, 0, 16) > 0
     assert ws(8, 4096, 4096) <= ws(16, 4096, 4096) <= ws(16, 4096, 8192)
     assert a % 256 == 0
@@ -133,6 +135,22 @@ def test_prepare_and_gemm_validation(lib):
     e = lib.llm_int8_export_stages
     assert e(None, 0, 32, 64, 48, None, None, None, None, None, None, None) == WORKSPACE
     assert e(P, need, 32, 65, 48, None, None, None, None, None, None, None) == SHAPE
+
+
+def test_fp16w_validation(lib):
+    need = lib.llm_int8_workspace_bytes(32, 64, 48)
+    f = lib.llm_int8_linear_fp16w
+    assert f(P, P, P, None, 6.0, 32, 64, 48, P2, P, need, None) == INVALID   # no W
+    assert f(P, P, P, MIS, 6.0, 32, 64, 48, P2, P, need, None) == ALIGN
+    assert f(P, P, P, P, math.nan, 32, 64, 48, P2, P, need, None) == INVALID
+    assert f(P, P, P, P, 6.0, 32, 72, 48, P2, P, need, None) == SHAPE
+    assert f(None, None, None, None, 6.0, 0, 64, 48, None, None, 0, None) == OK
+    g = lib.llm_int8_gemm_fp16w
+    assert g(P, P, None, 32, 64, 48, P2, None, P, need, None) == INVALID
+    assert g(P, P, MIS, 32, 64, 48, P2, None, P, need, None) == ALIGN
+    p = lib.llm_int8_prepare_fp16w
+    assert p(P, None, 6.0, 32, 64, 48, P, need, None) == INVALID
+    assert p(P, MIS, 6.0, 32, 64, 48, P, need, None) == ALIGN
 
 
 def test_python_binding_rejects_cpu_tensors(lib):
