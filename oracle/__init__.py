@@ -67,6 +67,11 @@ def lib():
         L.oracle_linear.argtypes = [_u16p, _i8p, _f32p, _u16p, ctypes.c_double,
                                     _i64, _i64, _i64, _u16p,
                                     _u8p, _i32p, _i32p, _i8p, _f32p, _i32p]
+        L.oracle_sq_factors.argtypes = [_f32p, _f32p, ctypes.c_double, _i64, _f32p]
+        L.oracle_column_absmax.argtypes = [_u16p, _i64, _i64, _f32p]
+        L.oracle_sq_quantize_weight.argtypes = [_u16p, _f32p, _i64, _i64, _i8p, _f32p]
+        L.oracle_sq_quantize_rows.argtypes = [_u16p, _f32p, _i64, _i64, _i8p, _f32p]
+        L.oracle_sq_output.argtypes = [_i32p, _f32p, _f32p, _i64, _i64, _u16p]
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -224,3 +229,64 @@ def linear_rows(X, Wq, sW, threshold: float, rows, W16=None):
     acc = int8_gemm(Xq, Wq)
     Y = decomposed_output(Xr, acc, sX, Wq, sW, idx, W16=W16)
     return Y, idx, Xq, sX, acc
+
+
+# --------------------------------------------------------------------------
+# SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1): see oracle.c
+# --------------------------------------------------------------------------
+
+def column_absmax(X):
+    """max_t |X[t,j]| per column, fp32 [K]."""
+    X = _f16bits(X)
+    R, K = X.shape
+    out = np.empty(max(K, 1), np.float32)
+    lib().oracle_column_absmax(_p(X, _u16p), R, K, _p(out, _f32p))
+    return out[:K]
+
+
+def sq_factors(ax, aw, alpha: float):
+    """s_j = ax_j^alpha / aw_j^(1-alpha) in fp64, rounded to fp32 (1 where
+    either maximum is 0)."""
+    ax = np.ascontiguousarray(ax, dtype=np.float32)
+    aw = np.ascontiguousarray(aw, dtype=np.float32)
+    K = ax.shape[0]
+    s = np.empty(max(K, 1), np.float32)
+    lib().oracle_sq_factors(_p(ax, _f32p), _p(aw, _f32p), float(alpha), K, _p(s, _f32p))
+    return s[:K]
+
+
+def sq_quantize_weight(W, s):
+    """(Wq int8 [N,K], sW fp32 [N]) of the smoothed weight W * s."""
+    W = _f16bits(W)
+    N, K = W.shape
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    Wq = np.empty((N, K), np.int8)
+    sW = np.empty(max(N, 1), np.float32)
+    lib().oracle_sq_quantize_weight(_p(W, _u16p), _p(s, _f32p), N, K, _p(Wq, _i8p), _p(sW, _f32p))
+    return Wq, sW[:N]
+
+
+def sq_quantize_rows(X, s):
+    """(Xq int8 [R,K], sX fp32 [R]) of the smoothed activation X * fl32(1/s)."""
+    X = _f16bits(X)
+    R, K = X.shape
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    Xq = np.empty((R, K), np.int8)
+    sX = np.empty(max(R, 1), np.float32)
+    lib().oracle_sq_quantize_rows(_p(X, _u16p), _p(s, _f32p), R, K, _p(Xq, _i8p), _p(sX, _f32p))
+    return Xq, sX[:R]
+
+
+def sq_linear(X, s, Wq, sW, stages: bool = False):
+    """Y fp16 [R,N] of the smoothed W8A8 product (no outlier decomposition)."""
+    Xq, sX = sq_quantize_rows(X, s)
+    acc = int8_gemm(Xq, Wq)
+    R, N = acc.shape
+    Y = np.empty((R, N), np.uint16)
+    sW = np.ascontiguousarray(sW, dtype=np.float32)
+    lib().oracle_sq_output(_p(acc, _i32p), _p(np.ascontiguousarray(sX, np.float32), _f32p),
+                           _p(sW, _f32p), R, N, _p(Y, _u16p))
+    Y = Y.view(np.float16)
+    if not stages:
+        return Y
+    return dict(Y=Y, Xq=Xq, sX=sX, acc=acc)

@@ -20,6 +20,7 @@ rounding is innocuous); the helpers below rely on that.
 """
 from __future__ import annotations
 
+import math
 import struct
 
 
@@ -92,3 +93,35 @@ def linear(Xbits, Wq, sW, threshold: float, Wbits=None):
             yrow.append(f2h(d + e))
         Y.append(yrow)
     return dict(flags=flags, idx=idx, Xq=Xq, sX=sX, acc=acc, Y_bits=Y)
+
+
+def sq_linear(Xbits, Wbits, X_cal_bits, alpha: float):
+    """SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1), every
+    step in Python: per-channel factors from the calibration rows and the
+    weight, the smoothed weight and activation, absmax int8 on both, exact
+    integer products.  Returns dict(s, Wq, sW, Xq, sX, acc, Y_bits)."""
+    K = len(Wbits[0])
+    ax = [max([abs(h2f(r[j])) for r in X_cal_bits] + [0.0]) for j in range(K)]
+    aw = [max([abs(h2f(r[j])) for r in Wbits] + [0.0]) for j in range(K)]
+    s = []
+    for j in range(K):
+        if ax[j] == 0.0 or aw[j] == 0.0:
+            s.append(1.0)
+        else:
+            s.append(f32(math.pow(ax[j], alpha) / math.pow(aw[j], 1.0 - alpha)))
+    Wq, sW = [], []
+    for row in Wbits:
+        ws = [f32(h2f(b) * s[j]) for j, b in enumerate(row)]
+        sc = f32(max([abs(v) for v in ws] + [0.0]) / 127.0)
+        sW.append(sc)
+        Wq.append([code(v, sc) if sc > 0.0 else 0 for v in ws])
+    Xq, sX = [], []
+    for row in Xbits:
+        xs = [f32(h2f(b) * f32(1.0 / s[j])) for j, b in enumerate(row)]
+        sc = f32(max([abs(v) for v in xs] + [0.0]) / 127.0)
+        sX.append(sc)
+        Xq.append([code(v, sc) if sc > 0.0 else 0 for v in xs])
+    acc = [[sum(a * b for a, b in zip(xr, wr)) for wr in Wq] for xr in Xq]
+    Y = [[f2h(f32(f32(float(acc[t][n]) * sX[t]) * sW[n])) for n in range(len(Wq))]
+         for t in range(len(Xq))]
+    return dict(s=s, Wq=Wq, sW=sW, Xq=Xq, sX=sX, acc=acc, Y_bits=Y)

@@ -309,3 +309,109 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/*
+ * SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1): the exact
+ * rewrite x . W^T = (x / s) . (W * s)^T with one factor s_j per input
+ * channel moves quantization difficulty from the activation to the weight;
+ * then both are quantized to int8 with the same absmax scheme as above and
+ * multiplied with no outlier decomposition.
+ *
+ * Readings (the printed factor formula is garbled):
+ *   s_j = ax_j^alpha / aw_j^(1-alpha), ax_j = max_t |X_cal[t,j]| over a
+ *   calibration batch, aw_j = max_n |W[n,j]|; computed in fp64, rounded to
+ *   fp32; s_j = 1 when ax_j or aw_j is 0 (the channel carries nothing).
+ *   W'[n,j] = fl32(W[n,j] * s_j), then the weight absmax quantization.
+ *   X'[t,j] = fl32(X[t,j] * fl32(1 / s_j)), then the token absmax
+ *   quantization over all columns; Y = fp16(fl32(fl32(acc * sX') * sW')).
+ */
+void oracle_sq_factors(const float *ax, const float *aw, double alpha, int64_t K, float *s)
+{
+    for (int64_t j = 0; j < K; j++) {
+        if (ax[j] == 0.0f || aw[j] == 0.0f)
+            s[j] = 1.0f;
+        else
+            s[j] = (float)(pow((double)ax[j], alpha) / pow((double)aw[j], 1.0 - alpha));
+    }
+}
+
+/* max |X[t,j]| over the rows, per column, as fp32 (exact for fp16 values) */
+void oracle_column_absmax(const uint16_t *X, int64_t R, int64_t K, float *out)
+{
+    for (int64_t j = 0; j < K; j++) {
+        double m = 0.0;
+        for (int64_t t = 0; t < R; t++) {
+            double v = fabs(oracle_h2d(X[t * K + j]));
+            if (v > m)
+                m = v;
+        }
+        out[j] = (float)m;
+    }
+}
+
+/* absmax code of an fp32 value for scale s (s > 0): rne(fl32(r / s)),
+   clamped to [-127, 127] */
+static int8_t sq_code(float r, float s)
+{
+    float q = rintf(r / s);
+    if (q > 127.0f)
+        q = 127.0f;
+    if (q < -127.0f)
+        q = -127.0f;
+    return (int8_t)q;
+}
+
+void oracle_sq_quantize_weight(const uint16_t *W, const float *s, int64_t N, int64_t K,
+                               int8_t *Wq, float *sW)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        float a = 0.0f;
+        for (int64_t j = 0; j < K; j++) {
+            float w = (float)oracle_h2d(W[n * K + j]) * s[j];
+            if (fabsf(w) > a)
+                a = fabsf(w);
+        }
+        const float sc = a / 127.0f;
+        sW[n] = sc;
+        for (int64_t j = 0; j < K; j++) {
+            float w = (float)oracle_h2d(W[n * K + j]) * s[j];
+            Wq[n * K + j] = sc > 0.0f ? sq_code(w, sc) : 0;
+        }
+    }
+}
+
+/* token side: smoothed codes and scales of rows X[0..R) */
+void oracle_sq_quantize_rows(const uint16_t *X, const float *s, int64_t R, int64_t K,
+                             int8_t *Xq, float *sX)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < R; t++) {
+        float a = 0.0f;
+        for (int64_t j = 0; j < K; j++) {
+            float x = (float)oracle_h2d(X[t * K + j]) * (1.0f / s[j]);
+            if (fabsf(x) > a)
+                a = fabsf(x);
+        }
+        const float sc = a / 127.0f;
+        sX[t] = sc;
+        for (int64_t j = 0; j < K; j++) {
+            float x = (float)oracle_h2d(X[t * K + j]) * (1.0f / s[j]);
+            Xq[t * K + j] = sc > 0.0f ? sq_code(x, sc) : 0;
+        }
+    }
+}
+
+/* Y = fp16(fl32(fl32(acc * sX) * sW)) (no outlier term) */
+void oracle_sq_output(const int32_t *acc, const float *sX, const float *sW, int64_t R, int64_t N,
+                      uint16_t *Y)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < R; t++) {
+        for (int64_t n = 0; n < N; n++) {
+            float d = (float)acc[t * N + n] * sX[t];
+            d = d * sW[n];
+            Y[t * N + n] = oracle_d2h((double)d);
+        }
+    }
+}

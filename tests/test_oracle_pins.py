@@ -487,3 +487,103 @@ def test_fp16w_brute_force_agrees_bit_exactly(case):
     r = oracle.linear(X, Wq, sW, thr, W16=W)
     b = brute.linear(X.view(np.uint16).tolist(), bWq, bsW, thr, Wbits=W.view(np.uint16).tolist())
     assert np.array_equal(r.view(np.uint16), np.array(b["Y_bits"], np.uint16).reshape(r.shape))
+
+
+# --------------------------------------------------------------------------
+# SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1): x.W^T =
+# (x/s).(W*s)^T with per-channel factors, then absmax int8 on both sides
+# --------------------------------------------------------------------------
+
+def _sq_full(X, W, alpha, X_cal=None):
+    X_cal = X if X_cal is None else X_cal
+    s = oracle.sq_factors(oracle.column_absmax(X_cal), oracle.column_absmax(W), alpha)
+    Wq, sW = oracle.sq_quantize_weight(W, s)
+    r = oracle.sq_linear(X, s, Wq, sW, stages=True)
+    r.update(s=s, Wq=Wq, sW=sW)
+    return r
+
+
+def test_sq_uniform_power_of_two_factor_is_the_plain_int8_path():
+    """A factor 2^k shared by every channel scales X, W and both scales by
+    exact powers of two: codes, accumulators and Y equal the plain
+    vector-wise int8 product (itself pinned to numpy above)."""
+    X, W, _ = workloads.make("tiny")
+    Wq0, sW0 = oracle.quantize_weight(W)
+    Y0 = oracle.linear(X, Wq0, sW0, np.inf)
+    for k in (-3, 0, 5):
+        s = np.full(X.shape[1], 2.0 ** k, np.float32)
+        Wq, sW = oracle.sq_quantize_weight(W, s)
+        assert np.array_equal(Wq, Wq0) and np.array_equal(sW, sW0 * np.float32(2.0 ** k))
+        Y = oracle.sq_linear(X, s, Wq, sW)
+        assert np.array_equal(Y.view(np.uint16), Y0.view(np.uint16)), k
+
+
+def test_sq_factors_closed_forms():
+    """alpha = 1 gives s = ax, alpha = 0 gives s = 1/aw, alpha = 0.5 gives
+    sqrt(ax/aw); a channel whose activation or weight maximum is 0 keeps 1."""
+    ax = np.array([8.0, 0.5, 0.0, 3.0, 100.0], np.float32)
+    aw = np.array([0.5, 2.0, 1.0, 0.0, 0.04], np.float32)
+    live = (ax > 0) & (aw > 0)
+    s1 = oracle.sq_factors(ax, aw, 1.0)
+    assert np.array_equal(s1, np.where(live, ax, 1.0).astype(np.float32))
+    s0 = oracle.sq_factors(ax, aw, 0.0)
+    inv = 1.0 / np.where(live, aw.astype(np.float64), 1.0)
+    assert np.array_equal(s0, np.where(live, inv, 1.0).astype(np.float32))
+    s5 = oracle.sq_factors(ax, aw, 0.5)
+    ref = np.sqrt(np.where(live, ax.astype(np.float64), 1.0) / np.where(live, aw.astype(np.float64), 1.0))
+    assert np.all(ulp32(s5, np.where(live, ref, 1.0).astype(np.float32)) <= 1)
+
+
+def ulp32(a, b):
+    ia = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    ib = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+def test_sq_half_migration_balances_channel_ranges():
+    """With alpha = 0.5 and the call's own X as calibration, each channel's
+    range becomes sqrt(ax * aw) on both sides."""
+    X, W, _ = workloads.make("tiny")
+    ax, aw = oracle.column_absmax(X), oracle.column_absmax(W)
+    s = oracle.sq_factors(ax, aw, 0.5)
+    xs = np.abs(X.astype(np.float32) * (np.float32(1.0) / s)).max(0)
+    ws = np.abs(W.astype(np.float32) * s).max(0)
+    target = np.sqrt(ax.astype(np.float64) * aw.astype(np.float64))
+    ok = (ax > 0) & (aw > 0)
+    assert np.allclose(xs[ok], target[ok], rtol=1e-6) and np.allclose(ws[ok], target[ok], rtol=1e-6)
+
+
+def test_sq_error_bound_and_benefit():
+    """|Y - X W^T| within the absmax bound of the smoothed operands, and
+    smoothing beats the plain int8 product on channel outliers."""
+    X, W, _ = workloads.make("tiny")
+    r = _sq_full(X, W, 0.5)
+    s = r["s"].astype(np.float64)
+    xs = X.astype(np.float64) * (1.0 / s)
+    ws = W.astype(np.float64) * s
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    sX = r["sX"].astype(np.float64)
+    sW = r["sW"].astype(np.float64)
+    K = X.shape[1]
+    bound = (np.abs(xs).sum(1)[:, None] * sW[None, :] / 2 + sX[:, None] * np.abs(ws).sum(1)[None, :] / 2
+             + K * sX[:, None] * sW[None, :] / 4)
+    y = r["Y"].astype(np.float64)
+    assert np.all(np.abs(y - exact) <= bound * (1 + 1e-5) + np.abs(y) * 2.0 ** -10 + 2.0 ** -24)
+    Wq0, sW0 = oracle.quantize_weight(W)
+    plain = oracle.linear(X, Wq0, sW0, np.inf).astype(np.float64)
+    assert np.abs(y - exact).mean() < 0.5 * np.abs(plain - exact).mean()
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(_case(), st.sampled_from([0.0, 0.5, 0.8, 1.0]))
+def test_sq_brute_force_agrees_bit_exactly(case, alpha):
+    X, W, _ = case
+    r = _sq_full(X, W, alpha)
+    b = brute.sq_linear(X.view(np.uint16).tolist(), W.view(np.uint16).tolist(),
+                        X.view(np.uint16).tolist(), alpha)
+    assert np.array_equal(r["s"], np.array(b["s"], np.float32))
+    assert np.array_equal(r["Wq"], np.array(b["Wq"], np.int8).reshape(r["Wq"].shape))
+    assert np.array_equal(r["sW"], np.array(b["sW"], np.float32))
+    assert np.array_equal(r["Xq"], np.array(b["Xq"], np.int8).reshape(r["Xq"].shape))
+    assert np.array_equal(r["sX"], np.array(b["sX"], np.float32))
+    assert np.array_equal(r["Y"].view(np.uint16), np.array(b["Y_bits"], np.uint16).reshape(r["Y"].shape))
