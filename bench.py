@@ -45,8 +45,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--threshold", type=float, default=None)
-    ap.add_argument("--variant", choices=["int8w", "fp16w"], default="int8w",
-                    help="outlier columns times the dequantized codes (default) or the fp16 weight")
+    ap.add_argument("--variant", choices=["int8w", "fp16w", "sq"], default="int8w",
+                    help="outlier columns times the dequantized codes (default) or the fp16 "
+                         "weight; sq: the SmoothQuant-style W8A8 call (smoothquant_linear, "
+                         "alpha 0.5, calibrated on the first 512 rows of X)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables it)")
     ap.add_argument("--no-reference", action="store_true",
@@ -71,28 +73,44 @@ def kernel_traffic(kind: str, path_src: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(X, W, w, target_s: float):
-    """The oracle on a bounded sample: detection over all of X (the outlier
-    set needs every row), then quantization, the int8 product and the output
-    for the first R rows, R sized so the run takes about target_s."""
+def cpu_baseline(X, W, w, target_s: float, variant: str, thr: float):
+    """The oracle on a bounded sample, R rows sized so the run takes about
+    target_s.  LLM.int8(): detection over all of X (the outlier set needs
+    every row), then quantization, the int8 product and the output for the
+    first R rows.  sq: the smoothed token quantization, int8 product and
+    output for the first R rows (the factors and the weight are offline)."""
     import numpy as np
 
     import oracle
-    Wq, sW = oracle.quantize_weight(W)
     cores = oracle.num_threads()
+    if variant == "sq":
+        s = oracle.sq_factors(oracle.column_absmax(X[:512]), oracle.column_absmax(W), 0.5)
+        Wq, sW = oracle.sq_quantize_weight(W, s)
+
+        def run(rows):
+            oracle.sq_linear(X[:rows], s, Wq, sW)
+        what = "smoothed quantization, int8 product and output for the first {r} of {T} rows"
+    else:
+        Wq, sW = oracle.quantize_weight(W)
+        W16 = W if variant == "fp16w" else None
+
+        def run(rows):
+            oracle.linear_rows(X, Wq, sW, thr, np.arange(rows), W16=W16)
+        what = ("detection over all {T} rows of X, then quantization, int8 product and "
+                "output for the first {r} of {T} rows")
     # grow the sample until one run takes a noticeable time, then size the
     # final sample for about target_s (the per-row cost dominates by then)
     rows, dt = 4, 0.0
     while rows < w.T:
         t0 = time.perf_counter()
-        oracle.linear_rows(X, Wq, sW, w.threshold, np.arange(rows))
+        run(rows)
         dt = time.perf_counter() - t0
         if dt >= target_s / 8:
             break
         rows = min(w.T, rows * 4)
     rows = int(min(w.T, max(4, rows * target_s / max(dt, 1e-3))))
     t0 = time.perf_counter()
-    oracle.linear_rows(X, Wq, sW, w.threshold, np.arange(rows))
+    run(rows)
     dt = time.perf_counter() - t0
     ops = 2.0 * rows * w.N * w.K
     return {
@@ -100,9 +118,7 @@ def cpu_baseline(X, W, w, target_s: float):
         "unit": "TOPS",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"detection over all {w.T} rows of X, then quantization, int8 product "
-                   f"and output for the first {rows} of {w.T} rows ({rows}x{w.K}x{w.N}); "
-                   f"{dt:.1f} s"),
+        "sample": what.format(r=rows, T=w.T) + f" ({rows}x{w.K}x{w.N}); {dt:.1f} s",
     }
 
 
@@ -131,7 +147,23 @@ def main():
     Y = torch.empty((T, N), dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
 
-    if args.variant == "fp16w":
+    if args.variant == "sq":
+        # offline, once per layer: factors from a calibration batch (the first
+        # 512 token rows) and the weight's column maxima; smoothed weight codes
+        ax = li8.smoothquant_column_absmax(X[:512])
+        s_f, s_inv = li8.smoothquant_factors(ax, li8.smoothquant_column_absmax(W), 0.5)
+        Wq, sW = li8.smoothquant_quantize_weight(W, s_f)
+        torch.cuda.synchronize()
+
+        def call():
+            li8.smoothquant_linear(X, s_inv, Wq, sW, out=Y, workspace=ws)
+
+        def prep():
+            li8.smoothquant_prepare(X, s_inv, N, ws)
+
+        def gemm():
+            li8.gemm(Wq, sW, T, ws, out=Y)
+    elif args.variant == "fp16w":
         def call():
             li8.linear_fp16w(X, Wq, sW, W, thr, out=Y, workspace=ws)
 
@@ -226,6 +258,9 @@ def main():
     # reads X, writes Xq, sX and the gathered outlier columns of X; the weight
     # gather reads and writes nO16 bytes per weight row
     prep_bytes = 2 * T * K + 2 * T * K + T * K + 4 * T + 2 * T * nO16 + 2 * N * nO16
+    if args.variant == "sq":
+        # one pass: reads X and the factors' reciprocals, writes Xq and sX
+        prep_bytes = 2 * T * K + 4 * K + T * K + 4 * T
     prep_gbps = prep_bytes / (prep_ms * 1e-3) / 1e9
 
     reference = None
@@ -261,7 +296,16 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    if few:
+    if few and args.variant == "sq":
+        # prepare kernel + the few-token GEMM on its workspace; the GEMM
+        # stage streams Wq once
+        gemm_bytes = N * K + T * K + 4 * T + 2 * T * N + 4 * N
+        gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm",
+                    "kernel": "k_decode (few-token GEMM on the workspace, no outliers)",
+                    "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None}
+    elif few:
         # one fused kernel is the whole call; it streams Wq once
         src = os.path.join(ROOT, "int8_matmul_amd", "csrc", "decode.hip")
         call_bytes = N * K + 2 * T * K + 2 * T * N + 4 * N
@@ -271,17 +315,19 @@ def main():
                               "int8 MFMA, outlier MFMA, epilogue)",
                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                    "traffic": kernel_traffic("decode", src)}
+                    "traffic": kernel_traffic("decode", src) if args.variant == "int8w" else None}
     else:
         src = os.path.join(ROOT, "int8_matmul_amd", "csrc", "gemm.hip")
         roofline = {"bound": "mfma",
                     "kernel": "k_gemm (int8 MFMA GEMM + dequant/outlier epilogue)",
                     "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
-                    "traffic": kernel_traffic("gemm", src)}
+                    # counters taken on the LLM.int8() call only
+                    "traffic": kernel_traffic("gemm", src) if args.variant == "int8w" else None}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.variant != "sq" else METRIC.replace("llm_int8_linear",
+                                                                      "smoothquant_linear"),
         "value": round(tops, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -289,7 +335,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "gpu_ms_per_step": round(gpu_ms_step, 5),
-        "timing": "one HIP graph of `steps` llm_int8_linear calls, wall clock between "
+        "timing": f"one HIP graph of `steps` {'smoothquant' if args.variant == 'sq' else 'llm_int8'}"
+                  "_linear calls, wall clock between "
                   "synchronizations; output checked against an eager call",
         "higher_is_better": True,
         "scaling": "weak",
@@ -297,10 +344,14 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": w.desc, "name": args.workload, "T": T, "K": K, "N": N,
-                   "threshold": thr, "n_outliers": nO, "outlier_weight": args.variant,
+                   "threshold": None if args.variant == "sq" else thr, "n_outliers": nO,
+                   "outlier_weight": args.variant if args.variant != "sq" else None,
+                   "method": ("SmoothQuant-style W8A8, alpha 0.5" if args.variant == "sq"
+                              else "LLM.int8() decomposition"),
                    "parallelism": "single GPU"},
         "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
-        "path": "few-token fused kernel" if few else "prepare kernels + tiled GEMM",
+        "path": ("few-token fused kernel" if few and args.variant != "sq" else
+                 "prepare kernel + few-token GEMM" if few else "prepare kernels + tiled GEMM"),
         "prepare_us": round(prep_ms * 1e3, 2),
         "gemm_us": round(gemm_ms * 1e3, 2),
         "quant_gbps": round(prep_gbps, 1),
@@ -309,7 +360,7 @@ def main():
         "roofline": roofline,
     }
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(X_np, W_np, w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(X_np, W_np, w, args.cpu_seconds, args.variant, thr)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

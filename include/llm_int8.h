@@ -170,6 +170,73 @@ li8_status llm_int8_gemm_fp16w(const int8_t *Wq, const float *sW, const void *W,
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1): instead of
+ * splitting off the outlier columns, one factor s_j per input feature moves
+ * their range from the activation to the weight through the exact rewrite
+ * X . W^T = (X / s) . (W * s)^T; both sides are then quantized with the
+ * absmax scheme above and multiplied in int8, with no floating-point part.
+ * The section gives the factor's formula garbled; it is read here as
+ *   s_j = ax_j^alpha / aw_j^(1 - alpha)
+ * with ax_j = max_t |X_cal[t,j]| over a calibration batch of activations,
+ * aw_j = max_n |W[n,j]|, and the migration strength alpha in [0, 1].
+ * Offline, once per layer: smoothquant_column_absmax (of the calibration
+ * batch and of W), smoothquant_factors, smoothquant_quantize_weight.  Per
+ * call: smoothquant_linear, or smoothquant_prepare + llm_int8_gemm.
+ */
+
+/*
+ * absmax[j] = max_r |A[r,j]| (exact, as fp32) for fp16 A [rows,K]; 0 for a
+ * column of zeros.  0 <= rows < 2^31 (rows*K may exceed 2^31); K as for
+ * every call.  absmax [K] fp32 out.
+ */
+li8_status smoothquant_column_absmax(const void *A, int64_t rows, int64_t K, float *absmax,
+                                     hipStream_t stream);
+
+/*
+ * The smoothing factors and their reciprocals, [K] fp32 each:
+ *   s[j]     = fl32(ax[j]^alpha / aw[j]^(1-alpha))  (evaluated in fp64),
+ *              or 1 where ax[j] or aw[j] is 0;
+ *   s_inv[j] = fl32(1 / s[j]).
+ * ax, aw [K] fp32 in (>= 0, finite); alpha in [0, 1], else
+ * LI8_ERR_INVALID_ARG.  The fp64 power is the device library's (within an
+ * ulp or so of fp64), so s[j] can differ from a correctly rounded
+ * evaluation only where the fp64 quotient lies that close to the midpoint
+ * of two fp32 values.
+ */
+li8_status smoothquant_factors(const float *ax, const float *aw, double alpha, int64_t K,
+                               float *s, float *s_inv, hipStream_t stream);
+
+/*
+ * Absmax quantization of the smoothed weight W' = fl32(W * s) (per column):
+ *   sW[n]   = fl32(max_k |W'[n,k]| / 127)
+ *   Wq[n,k] = clamp(rne(fl32(W'[n,k] / sW[n])), -127, 127)   (0 if sW[n] = 0)
+ * W [N,K] fp16 in, s [K] fp32 in, Wq [N,K] int8 out, sW [N] fp32 out.
+ */
+li8_status smoothquant_quantize_weight(const void *W, const float *s, int64_t N, int64_t K,
+                                       int8_t *Wq, float *sW, hipStream_t stream);
+
+/*
+ * Per-call token side: X' = fl32(X * s_inv) per column, then
+ *   sX[t]   = fl32(max_k |X'[t,k]| / 127)
+ *   Xq[t,k] = clamp(rne(fl32(X'[t,k] / sX[t])), -127, 127)   (0 if sX[t] = 0)
+ * written into `workspace` (sized by llm_int8_workspace_bytes(T, K, N)) with
+ * no outlier column, so that llm_int8_gemm on it computes
+ *   Y[t,n] = fp16(fl32(fl32(acc[t,n] * sX[t]) * sW[n])).
+ * X [T,K] fp16 in, s_inv [K] fp32 in (as written by smoothquant_factors).
+ */
+li8_status smoothquant_prepare(const void *X, const float *s_inv, int64_t T, int64_t K,
+                               int64_t N, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * The whole per-call layer: smoothquant_prepare followed by llm_int8_gemm
+ * (Wq, sW from smoothquant_quantize_weight).  Y [T,N] fp16 out.
+ */
+li8_status smoothquant_linear(const void *X, const float *s_inv, const int8_t *Wq,
+                              const float *sW, int64_t T, int64_t K, int64_t N, void *Y,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Copies the intermediate results of the last llm_int8_prepare on
  * `workspace` into caller buffers (device-to-device, on `stream`).  A test
  * hook: the product path never needs it.  Any output pointer may be NULL.

@@ -30,7 +30,8 @@ __all__ = [
     "Int8MatmulError", "LibraryNotBuilt", "library_path", "load_library",
     "quantize_weight", "workspace_bytes", "new_workspace", "linear", "prepare",
     "gemm", "export_stages", "few_token_path", "linear_fp16w", "prepare_fp16w",
-    "gemm_fp16w", "STATUS",
+    "gemm_fp16w", "smoothquant_column_absmax", "smoothquant_factors",
+    "smoothquant_quantize_weight", "smoothquant_prepare", "smoothquant_linear", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +104,16 @@ def load_library() -> ctypes.CDLL:
     L.llm_int8_prepare_fp16w.argtypes = [vp, vp, ctypes.c_float, i64, i64, i64, vp, sz, vp]
     L.llm_int8_gemm_fp16w.restype = ctypes.c_int
     L.llm_int8_gemm_fp16w.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    L.smoothquant_column_absmax.restype = ctypes.c_int
+    L.smoothquant_column_absmax.argtypes = [vp, i64, i64, vp, vp]
+    L.smoothquant_factors.restype = ctypes.c_int
+    L.smoothquant_factors.argtypes = [vp, vp, ctypes.c_double, i64, vp, vp, vp]
+    L.smoothquant_quantize_weight.restype = ctypes.c_int
+    L.smoothquant_quantize_weight.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    L.smoothquant_prepare.restype = ctypes.c_int
+    L.smoothquant_prepare.argtypes = [vp, vp, i64, i64, i64, vp, sz, vp]
+    L.smoothquant_linear.restype = ctypes.c_int
+    L.smoothquant_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]
     L.llm_int8_export_stages.restype = ctypes.c_int
     L.llm_int8_export_stages.argtypes = [vp, sz, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
     _lib = L
@@ -279,6 +290,92 @@ def gemm_fp16w(Wq: torch.Tensor, sW: torch.Tensor, W: torch.Tensor, T: int,
     _check("llm_int8_gemm_fp16w",
            L.llm_int8_gemm_fp16w(_ptr(Wq), _ptr(sW), _ptr(W), T, K, N, _ptr(out), _ptr(acc),
                                  _ptr(workspace), workspace.numel(), _stream(Wq.device)))
+    return out
+
+
+def smoothquant_column_absmax(A: torch.Tensor, out: torch.Tensor | None = None):
+    """max_r |A[r,j]| per column of fp16 A [rows,K], as fp32 [K]."""
+    L = load_library()
+    _require(A, torch.float16, "A", 2)
+    rows, K = A.shape
+    if out is None:
+        out = torch.empty((K,), dtype=torch.float32, device=A.device)
+    _require(out, torch.float32, "out", 1)
+    _check("smoothquant_column_absmax",
+           L.smoothquant_column_absmax(_ptr(A), rows, K, _ptr(out), _stream(A.device)))
+    return out
+
+
+def smoothquant_factors(ax: torch.Tensor, aw: torch.Tensor, alpha: float = 0.5):
+    """(s, s_inv) fp32 [K]: s_j = ax_j^alpha / aw_j^(1-alpha) (1 where either
+    maximum is 0) and fl32(1/s_j)."""
+    L = load_library()
+    _require(ax, torch.float32, "ax", 1)
+    _require(aw, torch.float32, "aw", 1)
+    K = ax.shape[0]
+    if aw.shape[0] != K:
+        raise ValueError(f"shape mismatch: ax {tuple(ax.shape)}, aw {tuple(aw.shape)}")
+    s = torch.empty((K,), dtype=torch.float32, device=ax.device)
+    s_inv = torch.empty((K,), dtype=torch.float32, device=ax.device)
+    _check("smoothquant_factors",
+           L.smoothquant_factors(_ptr(ax), _ptr(aw), float(alpha), K, _ptr(s), _ptr(s_inv),
+                                 _stream(ax.device)))
+    return s, s_inv
+
+
+def smoothquant_quantize_weight(W: torch.Tensor, s: torch.Tensor):
+    """(Wq int8 [N,K], sW fp32 [N]) of the smoothed weight fl32(W * s)."""
+    L = load_library()
+    _require(W, torch.float16, "W", 2)
+    _require(s, torch.float32, "s", 1)
+    N, K = W.shape
+    if s.shape[0] != K:
+        raise ValueError(f"shape mismatch: W {tuple(W.shape)}, s {tuple(s.shape)}")
+    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    sW = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check("smoothquant_quantize_weight",
+           L.smoothquant_quantize_weight(_ptr(W), _ptr(s), N, K, _ptr(Wq), _ptr(sW),
+                                         _stream(W.device)))
+    return Wq, sW
+
+
+def smoothquant_prepare(X: torch.Tensor, s_inv: torch.Tensor, N: int, workspace: torch.Tensor):
+    """Smoothed token codes and scales of X into `workspace` (no outlier
+    column); `gemm` on it then gives the smoothed W8A8 product."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(s_inv, torch.float32, "s_inv", 1)
+    T, K = X.shape
+    if s_inv.shape[0] != K:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, s_inv {tuple(s_inv.shape)}")
+    ws = _ws(workspace, T, K, N, X.device)
+    _check("smoothquant_prepare",
+           L.smoothquant_prepare(_ptr(X), _ptr(s_inv), T, K, N, _ptr(ws), ws.numel(),
+                                 _stream(X.device)))
+    return ws
+
+
+def smoothquant_linear(X: torch.Tensor, s_inv: torch.Tensor, Wq: torch.Tensor,
+                       sW: torch.Tensor, out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None):
+    """Y fp16 [T,N] of the smoothed W8A8 product (SmoothQuant-style)."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(s_inv, torch.float32, "s_inv", 1)
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(sW, torch.float32, "sW", 1)
+    T, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or sW.shape[0] != N or s_inv.shape[0] != K:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, s_inv {tuple(s_inv.shape)}, "
+                         f"Wq {tuple(Wq.shape)}, sW {tuple(sW.shape)}")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    _require(out, torch.float16, "out", 2)
+    ws = _ws(workspace, T, K, N, X.device)
+    _check("smoothquant_linear",
+           L.smoothquant_linear(_ptr(X), _ptr(s_inv), _ptr(Wq), _ptr(sW), T, K, N, _ptr(out),
+                                _ptr(ws), ws.numel(), _stream(X.device)))
     return out
 
 

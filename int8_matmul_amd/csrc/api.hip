@@ -255,6 +255,87 @@ li8_status llm_int8_linear_fp16w(const void *X, const int8_t *Wq, const float *s
                          workspace, stream);
 }
 
+li8_status smoothquant_column_absmax(const void *A, int64_t rows, int64_t K, float *absmax,
+                                     hipStream_t stream)
+{
+    li8_status st = check_shape(1, K, 1);
+    if (st != LI8_OK)
+        return st;
+    if (rows < 0 || rows >= ((int64_t)1 << 31))
+        return LI8_ERR_SHAPE;
+    if (K == 0)
+        return LI8_OK;
+    if ((rows > 0 && !A) || !absmax)
+        return LI8_ERR_INVALID_ARG;
+    if (misaligned(A) || misaligned(absmax))
+        return LI8_ERR_ALIGN;
+    return from_hip(
+        launch_column_absmax(static_cast<const uint16_t *>(A), rows, K, absmax, stream));
+}
+
+li8_status smoothquant_factors(const float *ax, const float *aw, double alpha, int64_t K,
+                               float *s, float *s_inv, hipStream_t stream)
+{
+    li8_status st = check_shape(1, K, 1);
+    if (st != LI8_OK)
+        return st;
+    if (!(alpha >= 0.0 && alpha <= 1.0))
+        return LI8_ERR_INVALID_ARG;
+    if (K == 0)
+        return LI8_OK;
+    if (!ax || !aw || !s || !s_inv)
+        return LI8_ERR_INVALID_ARG;
+    if (misaligned(ax) || misaligned(aw) || misaligned(s) || misaligned(s_inv))
+        return LI8_ERR_ALIGN;
+    return from_hip(launch_sq_factors(ax, aw, alpha, K, s, s_inv, stream));
+}
+
+li8_status smoothquant_quantize_weight(const void *W, const float *s, int64_t N, int64_t K,
+                                       int8_t *Wq, float *sW, hipStream_t stream)
+{
+    li8_status st = check_shape(1, K, N);
+    if (st != LI8_OK)
+        return st;
+    if (N == 0)
+        return LI8_OK;
+    if ((K > 0 && (!W || !s || !Wq)) || !sW)
+        return LI8_ERR_INVALID_ARG;
+    if (misaligned(W) || misaligned(s) || misaligned(Wq) || misaligned(sW))
+        return LI8_ERR_ALIGN;
+    return from_hip(
+        launch_sq_quantize_weight(static_cast<const uint16_t *>(W), s, N, K, Wq, sW, stream));
+}
+
+li8_status smoothquant_prepare(const void *X, const float *s_inv, int64_t T, int64_t K,
+                               int64_t N, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    // the threshold is unused here; 0 passes the check
+    li8_status st = check_linear_args(X, reinterpret_cast<const int8_t *>(s_inv), 0.0f, T, K, N,
+                                      workspace, workspace_bytes);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    return from_hip(launch_sq_prepare(static_cast<const uint16_t *>(X), s_inv, T, K,
+                                      static_cast<char *>(workspace), ws_layout(T, K, N), stream));
+}
+
+li8_status smoothquant_linear(const void *X, const float *s_inv, const int8_t *Wq,
+                              const float *sW, int64_t T, int64_t K, int64_t N, void *Y,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    li8_status st = check_linear_args(X, reinterpret_cast<const int8_t *>(s_inv), 0.0f, T, K, N,
+                                      workspace, workspace_bytes);
+    if (st == LI8_OK)
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    hipError_t e = launch_sq_prepare(static_cast<const uint16_t *>(X), s_inv, T, K,
+                                     static_cast<char *>(workspace), ws_layout(T, K, N), stream);
+    if (e != hipSuccess)
+        return LI8_ERR_HIP;
+    return gemm_common(Wq, sW, nullptr, T, K, N, Y, nullptr, workspace, stream);
+}
+
 li8_status llm_int8_export_stages(const void *workspace, size_t workspace_bytes, int64_t T,
                                   int64_t K, int64_t N, uint32_t *outlier_bits,
                                   int32_t *n_outliers, int32_t *outlier_idx, int8_t *Xq,

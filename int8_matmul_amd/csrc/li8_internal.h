@@ -84,4 +84,17 @@ hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, const uint16_t 
                               int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
                               const WsLayout &L, hipStream_t s);
 
+// SmoothQuant-style W8A8 (smoothquant.hip).  Column absmax of fp16 A
+// [rows,K] as fp32; factors s and fl32(1/s); smoothed weight quantization;
+// the per-call token side, which leaves codes, scales and nO = 0 in the
+// workspace for launch_gemm / launch_decode_gemm.
+hipError_t launch_column_absmax(const uint16_t *A, int64_t rows, int64_t K, float *out,
+                                hipStream_t s);
+hipError_t launch_sq_factors(const float *ax, const float *aw, double alpha, int64_t K, float *sf,
+                             float *r, hipStream_t s);
+hipError_t launch_sq_quantize_weight(const uint16_t *W, const float *sf, int64_t N, int64_t K,
+                                     int8_t *Wq, float *sW, hipStream_t s);
+hipError_t launch_sq_prepare(const uint16_t *X, const float *r, int64_t T, int64_t K, char *ws,
+                             const WsLayout &L, hipStream_t s);
+
 } // namespace li8

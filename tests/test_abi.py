@@ -42,6 +42,8 @@ def test_header_declares_the_expected_entry_points():
         "li8_status_str", "int8_quantize_weight", "llm_int8_workspace_bytes",
         "llm_int8_linear", "llm_int8_prepare", "llm_int8_gemm", "llm_int8_export_stages",
         "llm_int8_linear_fp16w", "llm_int8_prepare_fp16w", "llm_int8_gemm_fp16w",
+        "smoothquant_column_absmax", "smoothquant_factors", "smoothquant_quantize_weight",
+        "smoothquant_prepare", "smoothquant_linear",
     ])
 
 
@@ -151,6 +153,43 @@ def test_fp16w_validation(lib):
     p = lib.llm_int8_prepare_fp16w
     assert p(P, None, 6.0, 32, 64, 48, P, need, None) == INVALID
     assert p(P, MIS, 6.0, 32, 64, 48, P, need, None) == ALIGN
+
+
+def test_smoothquant_validation(lib):
+    c = lib.smoothquant_column_absmax
+    assert c(P, 10, 72, P2, None) == SHAPE          # K % 16
+    assert c(P, -1, 64, P2, None) == SHAPE
+    assert c(P, 1 << 31, 64, P2, None) == SHAPE
+    assert c(None, 10, 64, P2, None) == INVALID
+    assert c(P, 10, 64, None, None) == INVALID
+    assert c(MIS, 10, 64, P2, None) == ALIGN
+    assert c(None, 10, 0, None, None) == OK         # K = 0: nothing to do
+    f = lib.smoothquant_factors
+    for bad in (-0.1, 1.5, math.nan):
+        assert f(P, P, bad, 64, P2, P2, None) == INVALID
+    assert f(P, None, 0.5, 64, P2, P2, None) == INVALID
+    assert f(P, P, 0.5, 64, P2, None, None) == INVALID
+    assert f(P, MIS, 0.5, 64, P2, P2, None) == ALIGN
+    assert f(P, P, 0.5, 40, P2, P2, None) == SHAPE
+    assert f(None, None, 0.5, 0, None, None, None) == OK
+    q = lib.smoothquant_quantize_weight
+    assert q(P, None, 48, 64, P2, P2, None) == INVALID
+    assert q(P, P, 48, 64, P2, MIS, None) == ALIGN
+    assert q(P, P, 48, 70, P2, P2, None) == SHAPE
+    assert q(None, None, 0, 64, None, None, None) == OK
+    need = lib.llm_int8_workspace_bytes(32, 64, 48)
+    p = lib.smoothquant_prepare
+    assert p(P, None, 32, 64, 48, P, need, None) == INVALID
+    assert p(P, MIS, 32, 64, 48, P, need, None) == ALIGN
+    assert p(P, P, 32, 64, 48, P, need - 1, None) == WORKSPACE
+    assert p(None, None, 0, 64, 48, None, 0, None) == OK
+    L = lib.smoothquant_linear
+    assert L(P, P, P, None, 32, 64, 48, P2, P, need, None) == INVALID   # no sW
+    assert L(P, P, P, P, 32, 64, 48, None, P, need, None) == INVALID    # no Y
+    assert L(P, P, P, P, 32, 64, 48, P2, None, need, None) == WORKSPACE
+    assert L(P, P, MIS, P, 32, 64, 48, P2, P, need, None) == ALIGN
+    assert L(P, P, P, P, 32, 65, 48, P2, P, need, None) == SHAPE
+    assert L(None, None, None, None, 32, 64, 0, None, None, 0, None) == OK
 
 
 def test_python_binding_rejects_cpu_tensors(lib):
