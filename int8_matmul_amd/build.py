@@ -53,6 +53,13 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # a kernel whose host-side launch stub was not emitted leaves an
+    # undefined symbol that only fails at load time: refuse it here
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    bad = [ln.split()[-1] for ln in und.stdout.splitlines() if "__device_stub__" in ln]
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the library: " + ", ".join(bad))
     os.replace(tmp, OUT)
     return OUT
 

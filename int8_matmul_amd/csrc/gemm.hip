@@ -63,6 +63,19 @@ __device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, void *lds,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LI8_LDS void *)lds, 16, voffset, soffset, 0, 0);
 }
 
+// B (4 or 16) bytes per lane from rsrc at voffset into LDS at lds + B*lane.
+// (Called from a device function: the builtin written inside a kernel's
+// lambda makes the host pass drop the kernel's launch stub.)
+template <int B>
+__device__ __forceinline__ void load_to_lds_n(__amdgpu_buffer_rsrc_t r, void *lds, int voffset)
+{
+    static_assert(B == 4 || B == 16, "bytes per lane");
+    if constexpr (B == 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LI8_LDS void *)lds, 4, voffset, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LI8_LDS void *)lds, 16, voffset, 0, 0, 0);
+}
+
 template <int CPR>
 __device__ __forceinline__ int swz(int row)
 {
@@ -101,7 +114,13 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     constexpr int LA = BM * CPR / NT, LB = BN * CPR / NT;   // loads per lane per stage
     constexpr int RS = FN * 32 + 8;            // epilogue staging row stride (halves)
     constexpr int STG = NW * (FM * 32) * RS * 2;
-    constexpr int LDSB = (NS * SSZ > STG) ? NS * SSZ : STG;
+    // Epilogue operands prefetched into LDS at entry, past the ring: token
+    // scales, feature scales and the first 16-column chunk of XO and WO.
+    // The staging rows may overlap them; the staging barrier orders that.
+    constexpr int WOE = F16W ? 2 : 1;          // bytes per WO element
+    constexpr int PF_SX = NS * SSZ, PF_SW = PF_SX + 4 * BM, PF_XO = PF_SW + 4 * BN;
+    constexpr int PF_WO = PF_XO + 32 * BM, PF_END = PF_WO + 16 * WOE * BN;
+    constexpr int LDSB = (PF_END > STG) ? PF_END : STG;
     static_assert(FM * WM * 32 == BM && FN * WN * 32 == BN, "tile shape");
     static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "loader shape");
     static_assert(KS % 2 == 0 && NS >= 2, "pipeline shape");
@@ -243,6 +262,41 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     for (int s = 0; s < NS; s++)
         if (s < nk)
             issue(s);
+    // epilogue prefetch (after the first stages, so that they land first);
+    // rows past T or N read zeros or clamp, and are never stored
+    const __amdgpu_buffer_rsrc_t rXO = make_rsrc(XO, (int)(2u * (unsigned)T * (unsigned)K));
+    const __amdgpu_buffer_rsrc_t rWO = make_rsrc(WO, (int)((unsigned)WOE * (unsigned)N * (unsigned)K));
+    {
+        auto prefetch = [&](__amdgpu_buffer_rsrc_t r, int off, auto bytes_c, int n, auto voff) {
+            constexpr int B = decltype(bytes_c)::value;   // bytes per lane
+#pragma unroll
+            for (int j0 = wid * 64; j0 < n; j0 += NT) {
+                const int c = j0 + lane;
+                if (c < n)
+                    load_to_lds_n<B>(r, lds + off + j0 * B, voff(c));
+            }
+        };
+        using B4 = std::integral_constant<int, 4>;
+        using B16 = std::integral_constant<int, 16>;
+        const int sxb = T < (1 << 29) ? 4 * T : 0x7fffffff;
+        const int swb = N < (1 << 29) ? 4 * N : 0x7fffffff;
+        prefetch(make_rsrc(sX, sxb), PF_SX, B4{}, BM,
+                 [&](int c) { return (int)(4u * (unsigned)(m0 + c)); });
+        prefetch(make_rsrc(sW, swb), PF_SW, B4{}, BN,
+                 [&](int c) { return (int)(4u * (unsigned)(n0 + c)); });
+        if (nO > 0) {   // then K >= 16: chunk 0 lies inside every row
+            prefetch(rXO, PF_XO, B16{}, 2 * BM, [&](int c) {
+                return (int)((unsigned)min(m0 + (c >> 1), T - 1) * (unsigned)K * 2u + 16u * (c & 1));
+            });
+            if constexpr (F16W)
+                prefetch(rWO, PF_WO, B16{}, 2 * BN, [&](int c) {
+                    return (int)((unsigned)min(n0 + (c >> 1), N - 1) * (unsigned)K * 2u + 16u * (c & 1));
+                });
+            else
+                prefetch(rWO, PF_WO, B16{}, BN,
+                         [&](int c) { return (int)((unsigned)min(n0 + c, N - 1) * (unsigned)K); });
+        }
+    }
     if (nk > 0) {
         wait_loads_barrier<0>();
         lread(0, 0, 0);
@@ -273,21 +327,21 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                         acc_out[(int64_t)t * N + n] = acc[a][b][r];
                 }
     }
-    // token scales and the first 16-column chunk of the outlier operands
-    // are requested together; the feature scales after the outlier loop
+    if (nk == 0)   // no stage barrier ran: let the prefetched operands land
+        wait_loads_barrier<0>();
+    // token scales from the prefetch
+    const int ltok = wm * FM * 32 + (lane & 31);                 // local token row
+    const int lfea = wn * FN * 32 + (lane & 31);                 // local weight row
     float sx[FM];
 #pragma unroll
     for (int a = 0; a < FM; a++)
-        sx[a] = sX[min(tok0 + 32 * a, T - 1)];
+        sx[a] = *reinterpret_cast<const float *>(lds + PF_SX + 4 * (ltok + 32 * a));
     // outlier operands, chunk c: lane l supplies 8 of the 16 columns
     // (8*(l/32)..) of the weight row of block b and the token row of block
     // a; buffer loads with a fixed per-lane offset and the chunk's offset
     // in the scalar operand
+    // (WO: int8 codes [N,K], or in the fp16-weight variant fp16 [N,K])
     const int nch = (nO + 15) >> 4;
-    const __amdgpu_buffer_rsrc_t rXO = make_rsrc(XO, (int)(2u * (unsigned)T * (unsigned)K));
-    // WO: int8 codes [N,K], or in the fp16-weight variant fp16 [N,K]
-    constexpr int WOE = F16W ? 2 : 1;   // bytes per element
-    const __amdgpu_buffer_rsrc_t rWO = make_rsrc(WO, (int)((unsigned)WOE * (unsigned)N * (unsigned)K));
     int voX[FM], voW[FN];
 #pragma unroll
     for (int a = 0; a < FM; a++)
@@ -314,30 +368,30 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                 ow[set][b] = __builtin_amdgcn_raw_buffer_load_b64(rWO, voW[b], c * 16, 0);
         }
     };
+    // chunk 0 from the prefetch
+    auto oload0 = [&]() {
+#pragma unroll
+        for (int a = 0; a < FM; a++)
+            ox[0][a] = *reinterpret_cast<const v8h *>(lds + PF_XO + (ltok + 32 * a) * 32 + khalf * 16);
+#pragma unroll
+        for (int b = 0; b < FN; b++) {
+            if constexpr (F16W)
+                ow16[0][b] = *reinterpret_cast<const v8h *>(lds + PF_WO + (lfea + 32 * b) * 32 + khalf * 16);
+            else
+                ow[0][b] = *reinterpret_cast<const v2u *>(lds + PF_WO + (lfea + 32 * b) * 16 + khalf * 8);
+        }
+    };
     if (nch > 0)
-        oload(0, 0);
+        oload0();
 
     // feature scales, four consecutive per float4
     float4 sw[FN][4];
-    auto load_sw = [&]() {
-        if ((N & 3) == 0) {   // 16-byte loads; a group starting below N ends below N
+    auto load_sw = [&]() {   // from the prefetch (fea0 - n0 is a multiple of 4)
 #pragma unroll
-            for (int b = 0; b < FN; b++)
+        for (int b = 0; b < FN; b++)
 #pragma unroll
-                for (int g = 0; g < 4; g++)
-                    sw[b][g] = *reinterpret_cast<const float4 *>(sW + min(fea0 + 32 * b + 8 * g, N - 4));
-        } else {
-#pragma unroll
-            for (int b = 0; b < FN; b++)
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    const int n = fea0 + 32 * b + 8 * g;
-                    sw[b][g].x = sW[min(n, N - 1)];
-                    sw[b][g].y = sW[min(n + 1, N - 1)];
-                    sw[b][g].z = sW[min(n + 2, N - 1)];
-                    sw[b][g].w = sW[min(n + 3, N - 1)];
-                }
-        }
+            for (int g = 0; g < 4; g++)
+                sw[b][g] = *reinterpret_cast<const float4 *>(lds + PF_SW + 4 * (fea0 - n0 + 32 * b + 8 * g));
     };
     // D = fl32(acc * sX); in the fp16-weight variant D = fl32(D * sW) here,
     // before the outlier product (which is then in output units)
@@ -389,18 +443,18 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
             for (int b = 0; b < FN; b++)
                 d[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wb[b], ox[set][a], d[a][b], 0, 0, 0);
     };
-    // two chunks per iteration; a chunk index past the end re-reads the
-    // last chunk (a valid address) and is masked
-    // (the scheduling barriers keep the compiler from moving the loads
-    // down next to their use)
-    for (int c = 0; c < nch; c += 2) {
-        oload(1, min(c + 1, nch - 1));
-        __builtin_amdgcn_sched_barrier(0);
+    // chunk 0 (from the prefetch), then two chunks per iteration with both
+    // loads in flight together; a chunk index past the end re-reads the
+    // last chunk (a valid address) and is masked.  The scheduling barriers
+    // keep the compiler from moving the loads down next to their use.
+    if (nch > 0)
         omfma(0, ~0u);
+    for (int c = 1; c < nch; c += 2) {
+        oload(1, c);
+        oload(0, min(c + 1, nch - 1));
         __builtin_amdgcn_sched_barrier(0);
-        oload(0, min(c + 2, nch - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        omfma(1, (c + 1 < nch) ? ~0u : 0u);
+        omfma(1, ~0u);
+        omfma(0, (c + 1 < nch) ? ~0u : 0u);
         __builtin_amdgcn_sched_barrier(0);
     }
 
