@@ -23,7 +23,7 @@
 //    gets an out-of-range buffer offset, for which the hardware returns
 //    zeros, so a ragged K needs no branch.
 //  - MFMA fragments are double-buffered in registers: the LDS reads of
-//    k-step s+1 are issued before the MFMAs of k-step s.  The one barrier
+//    k-step s+1 are interleaved one-to-one with the MFMAs of k-step s.  The one barrier
 //    per stage sits before the MFMAs of the stage's last k-step, after all
 //    reads of the stage were issued, so the MFMA pipe has queued work when
 //    a wave reaches it.
@@ -239,17 +239,44 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
 #pragma unroll
         for (int kk = 0; kk < KS; kk++) {
             const int cur = kk & 1;
+            // Each fragment read of the next k-step is paired with one MFMA
+            // of this one, so that the reads do not arrive in a burst that
+            // the other wave on the SIMD must wait behind.  (The global ->
+            // LDS loads of the last k-step stay grouped: each needs its own
+            // M0 value, and the scheduler keeps them together.)
+            constexpr int NMF = FM * FN, NRD = FM + FN;
             if (kk + 1 < KS) {
+                __builtin_amdgcn_sched_barrier(0);
                 lread(cur ^ 1, kt, kk + 1);
+                mfmas(cur);
+#pragma unroll
+                for (int i = 0; i < NMF; i++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i < NRD)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             } else if constexpr (!LAST) {
                 wait_loads_barrier<WAIT>();   // stage kt+1 landed; stage kt read by all
                 if constexpr (ISSUE)
                     issue(kt + NS);
                 lread(cur ^ 1, kt + 1, 0);
+                mfmas(cur);
+                constexpr int NLD = ISSUE ? LA + LB : 0;
+#pragma unroll
+                for (int i = 0; i < NMF; i++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i < NRD)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (i < NLD)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(cur);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(cur);
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
     using TF = std::false_type;
