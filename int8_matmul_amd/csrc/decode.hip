@@ -282,7 +282,9 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     } else {
         // token codes of the prepared workspace into the LDS layout: up to
         // 16 chunks of 16 bytes per thread (T*K/16 <= 16*512)
-        nO = meta[0];
+        // clamped, so that a workspace no prepare call wrote (outside the
+        // contract) gives wrong values, not reads out of bounds
+        nO = min(max(meta[0], 0), K);
         const int nq = K / 16, tot = T * nq;
         uint4 st[kDMaxT];
 #pragma unroll
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         } else {
 #pragma unroll
             for (int e = 0; e < 8; e++)
-                col[e] = (i0 + e < nO) ? idx_g[i0 + e] : 0;
+                col[e] = (i0 + e < nO) ? min(max(idx_g[i0 + e], 0), K - 1) : 0;
         }
         const int64_t trow = (int64_t)min(tok, T - 1) * K;
 #pragma unroll

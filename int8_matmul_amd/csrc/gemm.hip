@@ -147,7 +147,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     // main loop: a scalar load in flight across it would make the compiler
     // wait for all LDS reads instead of the older half
     asm volatile("" ::"s"(sX), "s"(sW), "s"(XO), "s"(WO), "s"(Y), "s"(acc_out));
-    const int nO = meta[0];
+    const int nO = min(max(meta[0], 0), K);   // (a bad workspace cannot lengthen the loop)
     asm volatile("" ::"s"(nO));
 
     // ---- global -> LDS loaders: load i of this lane fills LDS chunk
