@@ -45,10 +45,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--threshold", type=float, default=None)
-    ap.add_argument("--variant", choices=["int8w", "fp16w", "sq"], default="int8w",
+    ap.add_argument("--variant", choices=["int8w", "fp16w", "sq", "cached"], default="int8w",
                     help="outlier columns times the dequantized codes (default) or the fp16 "
                          "weight; sq: the SmoothQuant-style W8A8 call (smoothquant_linear, "
-                         "alpha 0.5, calibrated on the first 512 rows of X)")
+                         "alpha 0.5, calibrated on the first 512 rows of X); cached: "
+                         "llm_int8_linear_cached with an outlier-column cache (every call "
+                         "after the first reuses the gathered weight columns)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables it)")
     ap.add_argument("--no-reference", action="store_true",
@@ -163,6 +165,17 @@ def main():
 
         def gemm():
             li8.gemm(Wq, sW, T, ws, out=Y)
+    elif args.variant == "cached":
+        cache = li8.new_cache(K, N, dev)
+
+        def call():
+            li8.linear_cached(X, Wq, sW, cache, thr, out=Y, workspace=ws)
+
+        def prep():
+            li8.prepare_cached(X, Wq, thr, ws, cache)
+
+        def gemm():
+            li8.gemm_cached(Wq, sW, T, ws, cache, out=Y)
     elif args.variant == "fp16w":
         def call():
             li8.linear_fp16w(X, Wq, sW, W, thr, out=Y, workspace=ws)
@@ -277,6 +290,9 @@ def main():
     # reads X, writes Xq, sX and the gathered outlier columns of X; the weight
     # gather reads and writes nO16 bytes per weight row
     prep_bytes = 2 * T * K + 2 * T * K + T * K + 4 * T + 2 * T * nO16 + 2 * N * nO16
+    if args.variant == "cached":
+        # the weight gather is skipped on a hit (every timed call)
+        prep_bytes = 2 * T * K + 2 * T * K + T * K + 4 * T + 2 * T * nO16
     if args.variant == "sq":
         # one pass: reads X and the factors' reciprocals, writes Xq and sX
         prep_bytes = 2 * T * K + 4 * K + T * K + 4 * T
@@ -344,9 +360,10 @@ def main():
                     # counters taken on the LLM.int8() call only
                     "traffic": kernel_traffic("gemm", src) if args.variant == "int8w" else None}
 
+    entry = {"sq": "smoothquant_linear", "cached": "llm_int8_linear_cached",
+             "fp16w": "llm_int8_linear_fp16w"}.get(args.variant, "llm_int8_linear")
     out = {
-        "metric": METRIC if args.variant != "sq" else METRIC.replace("llm_int8_linear",
-                                                                      "smoothquant_linear"),
+        "metric": METRIC.replace("llm_int8_linear", entry),
         "value": round(tops, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -354,8 +371,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "gpu_ms_per_step": round(gpu_ms_step, 5),
-        "timing": f"one HIP graph of `steps` {'smoothquant' if args.variant == 'sq' else 'llm_int8'}"
-                  "_linear calls, wall clock between "
+        "timing": f"one HIP graph of `steps` {entry} calls, wall clock between "
                   "synchronizations; output checked against an eager call",
         "higher_is_better": True,
         "scaling": "weak",
@@ -364,7 +380,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.desc, "name": args.workload, "T": T, "K": K, "N": N,
                    "threshold": None if args.variant == "sq" else thr, "n_outliers": nO,
-                   "outlier_weight": args.variant if args.variant != "sq" else None,
+                   "outlier_weight": ("int8w" if args.variant == "cached" else
+                                      args.variant if args.variant != "sq" else None),
+                   "outlier_cache": args.variant == "cached",
                    "method": ("SmoothQuant-style W8A8, alpha 0.5" if args.variant == "sq"
                               else "LLM.int8() decomposition"),
                    "parallelism": "single GPU"},

@@ -170,6 +170,55 @@ li8_status llm_int8_gemm_fp16w(const int8_t *Wq, const float *sW, const void *W,
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Outlier-column cache (lowentro.cn "model quantization" notes, Q4: the
+ * outlier features sit on the same few channels from token to token, so the
+ * set found by step 1 tends to repeat across calls).  A cache is a device
+ * buffer owned by the caller and bound to one quantized weight (Wq); it holds
+ * the last outlier set and the outlier columns of Wq gathered for it.  A call
+ * whose set equals the cached one skips that gather (which reads about all of
+ * Wq when the outlier columns are spread over K) and the GEMM reads the
+ * cached columns.  Detection still runs on every call, so the result is
+ * always that of llm_int8_linear, bit for bit, whatever the cache holds.
+ *
+ * Layout, for tests and inspection: the cache starts with int32 hdr[64],
+ * hdr[0] = 1 when it holds a set, hdr[1] = that set's nO, hdr[2] = calls
+ * that reused it (hits), hdr[3] = calls that gathered (misses); hits and
+ * misses count tiled calls only.  For few tokens (the fused path: T <= 16,
+ * K <= 8192) the cache is neither read nor written.
+ *
+ * Ownership: one cache per weight, and one call in flight per cache (calls
+ * that share it must be ordered, e.g. on one stream).  After Wq changes, or
+ * before first use, llm_int8_cache_reset must run; a cache used with a
+ * weight other than the one it was filled from gives wrong outputs.
+ */
+
+/* Bytes of a cache for a weight [N,K] (about N*K); 0 if the shape is invalid. */
+size_t llm_int8_cache_bytes(int64_t K, int64_t N);
+
+/* Marks the cache empty (and zeroes its counters); enqueued on `stream`. */
+li8_status llm_int8_cache_reset(void *cache, size_t cache_bytes, int64_t K, int64_t N,
+                                hipStream_t stream);
+
+/*
+ * llm_int8_linear with an outlier-column cache; same arguments, plus the
+ * cache (16-byte aligned, at least llm_int8_cache_bytes(K, N) bytes).
+ * Y is bit-identical to llm_int8_linear's.
+ */
+li8_status llm_int8_linear_cached(const void *X, const int8_t *Wq, const float *sW,
+                                  float threshold, int64_t T, int64_t K, int64_t N, void *Y,
+                                  void *workspace, size_t workspace_bytes, void *cache,
+                                  size_t cache_bytes, hipStream_t stream);
+
+/* The two halves of llm_int8_linear_cached (as llm_int8_prepare / _gemm). */
+li8_status llm_int8_prepare_cached(const void *X, const int8_t *Wq, float threshold, int64_t T,
+                                   int64_t K, int64_t N, void *workspace, size_t workspace_bytes,
+                                   void *cache, size_t cache_bytes, hipStream_t stream);
+li8_status llm_int8_gemm_cached(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
+                                void *Y, int32_t *acc, const void *workspace,
+                                size_t workspace_bytes, const void *cache, size_t cache_bytes,
+                                hipStream_t stream);
+
+/*
  * SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1): instead of
  * splitting off the outlier columns, one factor s_j per input feature moves
  * their range from the activation to the weight through the exact rewrite

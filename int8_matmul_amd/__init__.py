@@ -31,7 +31,9 @@ __all__ = [
     "quantize_weight", "workspace_bytes", "new_workspace", "linear", "prepare",
     "gemm", "export_stages", "few_token_path", "linear_fp16w", "prepare_fp16w",
     "gemm_fp16w", "smoothquant_column_absmax", "smoothquant_factors",
-    "smoothquant_quantize_weight", "smoothquant_prepare", "smoothquant_linear", "STATUS",
+    "smoothquant_quantize_weight", "smoothquant_prepare", "smoothquant_linear",
+    "cache_bytes", "new_cache", "cache_reset", "cache_stats", "linear_cached", "prepare_cached",
+    "gemm_cached", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -114,6 +116,18 @@ def load_library() -> ctypes.CDLL:
     L.smoothquant_prepare.argtypes = [vp, vp, i64, i64, i64, vp, sz, vp]
     L.smoothquant_linear.restype = ctypes.c_int
     L.smoothquant_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]
+    L.llm_int8_cache_bytes.restype = sz
+    L.llm_int8_cache_bytes.argtypes = [i64, i64]
+    L.llm_int8_cache_reset.restype = ctypes.c_int
+    L.llm_int8_cache_reset.argtypes = [vp, sz, i64, i64, vp]
+    L.llm_int8_linear_cached.restype = ctypes.c_int
+    L.llm_int8_linear_cached.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp, sz,
+                                         vp, sz, vp]
+    L.llm_int8_prepare_cached.restype = ctypes.c_int
+    L.llm_int8_prepare_cached.argtypes = [vp, vp, ctypes.c_float, i64, i64, i64, vp, sz, vp, sz,
+                                          vp]
+    L.llm_int8_gemm_cached.restype = ctypes.c_int
+    L.llm_int8_gemm_cached.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, sz, vp, sz, vp]
     L.llm_int8_export_stages.restype = ctypes.c_int
     L.llm_int8_export_stages.argtypes = [vp, sz, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
     _lib = L
@@ -290,6 +304,97 @@ def gemm_fp16w(Wq: torch.Tensor, sW: torch.Tensor, W: torch.Tensor, T: int,
     _check("llm_int8_gemm_fp16w",
            L.llm_int8_gemm_fp16w(_ptr(Wq), _ptr(sW), _ptr(W), T, K, N, _ptr(out), _ptr(acc),
                                  _ptr(workspace), workspace.numel(), _stream(Wq.device)))
+    return out
+
+
+def cache_bytes(K: int, N: int) -> int:
+    n = load_library().llm_int8_cache_bytes(K, N)
+    if n == 0:
+        raise Int8MatmulError("llm_int8_cache_bytes", 2)
+    return int(n)
+
+
+def new_cache(K: int, N: int, device) -> torch.Tensor:
+    """An empty outlier-column cache for a weight [N,K] (reset, ready to use)."""
+    c = torch.empty(cache_bytes(K, N), dtype=torch.uint8, device=device)
+    cache_reset(c, K, N)
+    return c
+
+
+def cache_reset(cache: torch.Tensor, K: int, N: int) -> torch.Tensor:
+    """Mark the cache empty; needed after its weight changes."""
+    L = load_library()
+    _require(cache, torch.uint8, "cache", 1)
+    _check("llm_int8_cache_reset",
+           L.llm_int8_cache_reset(_ptr(cache), cache.numel(), K, N, _stream(cache.device)))
+    return cache
+
+
+def cache_stats(cache: torch.Tensor) -> dict:
+    """valid, nO, hits, misses from the cache header (synchronizes)."""
+    h = cache[:16].view(torch.int32).cpu().tolist()
+    return dict(valid=h[0], nO=h[1], hits=h[2], misses=h[3])
+
+
+def linear_cached(X: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, cache: torch.Tensor,
+                  threshold: float = 6.0, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None):
+    """`linear` with an outlier-column cache bound to Wq (bit-identical Y)."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(sW, torch.float32, "sW", 1)
+    _require(cache, torch.uint8, "cache", 1)
+    T, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or sW.shape[0] != N:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, sW {tuple(sW.shape)}")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    _require(out, torch.float16, "out", 2)
+    ws = _ws(workspace, T, K, N, X.device)
+    _check("llm_int8_linear_cached",
+           L.llm_int8_linear_cached(_ptr(X), _ptr(Wq), _ptr(sW), float(threshold), T, K, N,
+                                    _ptr(out), _ptr(ws), ws.numel(), _ptr(cache), cache.numel(),
+                                    _stream(X.device)))
+    return out
+
+
+def prepare_cached(X: torch.Tensor, Wq: torch.Tensor, threshold: float, workspace: torch.Tensor,
+                   cache: torch.Tensor):
+    """`prepare` with an outlier-column cache."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(cache, torch.uint8, "cache", 1)
+    T, K = X.shape
+    N = Wq.shape[0]
+    ws = _ws(workspace, T, K, N, X.device)
+    _check("llm_int8_prepare_cached",
+           L.llm_int8_prepare_cached(_ptr(X), _ptr(Wq), float(threshold), T, K, N, _ptr(ws),
+                                     ws.numel(), _ptr(cache), cache.numel(), _stream(X.device)))
+    return ws
+
+
+def gemm_cached(Wq: torch.Tensor, sW: torch.Tensor, T: int, workspace: torch.Tensor,
+                cache: torch.Tensor, out: torch.Tensor | None = None,
+                acc: torch.Tensor | None = None):
+    """`gemm` on a workspace from `prepare_cached` with the same cache."""
+    L = load_library()
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(sW, torch.float32, "sW", 1)
+    _require(cache, torch.uint8, "cache", 1)
+    N, K = Wq.shape
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=Wq.device)
+    _require(out, torch.float16, "out", 2)
+    if acc is not None:
+        _require(acc, torch.int32, "acc", 2)
+    _require(workspace, torch.uint8, "workspace", 1)
+    _check("llm_int8_gemm_cached",
+           L.llm_int8_gemm_cached(_ptr(Wq), _ptr(sW), T, K, N, _ptr(out), _ptr(acc),
+                                  _ptr(workspace), workspace.numel(), _ptr(cache), cache.numel(),
+                                  _stream(Wq.device)))
     return out
 
 

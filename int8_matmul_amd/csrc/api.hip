@@ -97,17 +97,32 @@ li8_status check_gemm_args(const int8_t *Wq, const float *sW, int64_t T, int64_t
     return LI8_OK;
 }
 
-// W16 null: the int8 path; else the fp16-weight variant.
+// W16 null: the int8 path; else the fp16-weight variant.  cache: null, or
+// the outlier-column cache whose gathered columns the tiled GEMM reads.
 li8_status gemm_common(const int8_t *Wq, const float *sW, const uint16_t *W16, int64_t T,
                        int64_t K, int64_t N, void *Y, int32_t *acc, const void *workspace,
-                       hipStream_t stream)
+                       hipStream_t stream, const void *cache = nullptr)
 {
     const WsLayout L = ws_layout(T, K, N);
     if (decode_shape(T, K))
         return from_hip(launch_decode_gemm(Wq, sW, W16, T, K, N, static_cast<uint16_t *>(Y), acc,
                                            static_cast<const char *>(workspace), L, stream));
+    const int8_t *WO =
+        cache ? static_cast<const int8_t *>(cache) + cache_layout(K, N).WO : nullptr;
     return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), acc,
-                                static_cast<const char *>(workspace), L, W16 != nullptr, stream));
+                                static_cast<const char *>(workspace), L, W16 != nullptr, stream,
+                                WO));
+}
+
+li8_status check_cache(const void *cache, size_t cache_bytes, int64_t K, int64_t N)
+{
+    if (!cache)
+        return LI8_ERR_INVALID_ARG;
+    if (misaligned(cache))
+        return LI8_ERR_ALIGN;
+    if (cache_bytes < cache_layout(K, N).total)
+        return LI8_ERR_WORKSPACE;
+    return LI8_OK;
 }
 
 // W16 null: the int8 path; else the fp16-weight variant.
@@ -334,6 +349,79 @@ li8_status smoothquant_linear(const void *X, const float *s_inv, const int8_t *W
     if (e != hipSuccess)
         return LI8_ERR_HIP;
     return gemm_common(Wq, sW, nullptr, T, K, N, Y, nullptr, workspace, stream);
+}
+
+size_t llm_int8_cache_bytes(int64_t K, int64_t N)
+{
+    if (check_shape(1, K, N) != LI8_OK)
+        return 0;
+    return cache_layout(K, N).total;
+}
+
+li8_status llm_int8_cache_reset(void *cache, size_t cache_bytes, int64_t K, int64_t N,
+                                hipStream_t stream)
+{
+    li8_status st = check_shape(1, K, N);
+    if (st == LI8_OK)
+        st = check_cache(cache, cache_bytes, K, N);
+    if (st != LI8_OK)
+        return st;
+    return from_hip(launch_cache_reset(static_cast<char *>(cache), stream));
+}
+
+li8_status llm_int8_prepare_cached(const void *X, const int8_t *Wq, float threshold, int64_t T,
+                                   int64_t K, int64_t N, void *workspace, size_t workspace_bytes,
+                                   void *cache, size_t cache_bytes, hipStream_t stream)
+{
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    if (st == LI8_OK && T > 0 && N > 0)
+        st = check_cache(cache, cache_bytes, K, N);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    // few tokens: the workspace GEMM gathers the outlier weights by index
+    // itself; the cache is neither read nor written
+    const bool use = !decode_shape(T, K);
+    return from_hip(launch_prepare(static_cast<const uint16_t *>(X), Wq, nullptr,
+                                   threshold_magnitude(threshold), T, K, N,
+                                   static_cast<char *>(workspace), ws_layout(T, K, N), stream,
+                                   use ? static_cast<char *>(cache) : nullptr));
+}
+
+li8_status llm_int8_gemm_cached(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
+                                void *Y, int32_t *acc, const void *workspace,
+                                size_t workspace_bytes, const void *cache, size_t cache_bytes,
+                                hipStream_t stream)
+{
+    li8_status st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes);
+    if (st == LI8_OK && T > 0 && N > 0)
+        st = check_cache(cache, cache_bytes, K, N);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    return gemm_common(Wq, sW, nullptr, T, K, N, Y, acc, workspace, stream, cache);
+}
+
+li8_status llm_int8_linear_cached(const void *X, const int8_t *Wq, const float *sW,
+                                  float threshold, int64_t T, int64_t K, int64_t N, void *Y,
+                                  void *workspace, size_t workspace_bytes, void *cache,
+                                  size_t cache_bytes, hipStream_t stream)
+{
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    if (st == LI8_OK)
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
+    if (st == LI8_OK && T > 0 && N > 0)
+        st = check_cache(cache, cache_bytes, K, N);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    if (decode_shape(T, K))   // one fused kernel; the cache is not used
+        return linear_common(X, Wq, sW, nullptr, threshold, T, K, N, Y, workspace, stream);
+    const WsLayout L = ws_layout(T, K, N);
+    hipError_t e = launch_prepare(static_cast<const uint16_t *>(X), Wq, nullptr,
+                                  threshold_magnitude(threshold), T, K, N,
+                                  static_cast<char *>(workspace), L, stream,
+                                  static_cast<char *>(cache));
+    if (e != hipSuccess)
+        return LI8_ERR_HIP;
+    return gemm_common(Wq, sW, nullptr, T, K, N, Y, nullptr, workspace, stream, cache);
 }
 
 li8_status llm_int8_export_stages(const void *workspace, size_t workspace_bytes, int64_t T,

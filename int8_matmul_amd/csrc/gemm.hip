@@ -544,7 +544,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
 
 template <int BM, int BN, int BKS, int NS, int WM, int WN, int GM, bool F16W>
 hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
-                      uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, hipStream_t s)
+                      uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, hipStream_t s,
+                      const int8_t *WOx)
 {
     const int tiles_m = (int)((T + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
@@ -554,7 +555,7 @@ hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, i
     const float *sX = reinterpret_cast<const float *>(ws + L.sX);
     const int32_t *meta = reinterpret_cast<const int32_t *>(ws + L.meta);
     const uint16_t *XO = reinterpret_cast<const uint16_t *>(ws + L.XO);
-    const int8_t *WO = reinterpret_cast<const int8_t *>(ws + L.WO);
+    const int8_t *WO = WOx ? WOx : reinterpret_cast<const int8_t *>(ws + L.WO);
     if (acc)
         hipLaunchKernelGGL((k_gemm<BM, BN, BKS, NS, WM, WN, GM, F16W, true>), grid, block, 0, s, Xq, Wq,
                            sX, sW, meta, XO, WO, (int)T, (int)K, (int)N, tiles_m, tiles_n, Y, acc);
@@ -576,17 +577,17 @@ constexpr int kCUs = 256;
 
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
                        uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, bool fp16w,
-                       hipStream_t s)
+                       hipStream_t s, const int8_t *WO)
 {
     const int64_t tm = (T + 255) / 256;
     const int64_t big = tm * ((N + 255) / 256), small = tm * ((N + 127) / 128);
     const double cost_big = (double)((big + kCUs - 1) / kCUs);
     const double cost_small = 0.5 * 1.1 * (double)((small + kCUs - 1) / kCUs);
     if (cost_small < cost_big)
-        return fp16w ? launch_cfg<256, 128, 128, 2, 4, 2, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s)
-                     : launch_cfg<256, 128, 128, 2, 4, 2, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s);
-    return fp16w ? launch_cfg<256, 256, 128, 2, 2, 4, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s)
-                 : launch_cfg<256, 256, 128, 2, 2, 4, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s);
+        return fp16w ? launch_cfg<256, 128, 128, 2, 4, 2, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO)
+                     : launch_cfg<256, 128, 128, 2, 4, 2, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO);
+    return fp16w ? launch_cfg<256, 256, 128, 2, 2, 4, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO)
+                 : launch_cfg<256, 256, 128, 2, 2, 4, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO);
 }
 
 } // namespace li8

@@ -56,21 +56,48 @@ inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
     return L;
 }
 
+// Outlier-column cache, owned by the caller and bound to one Wq:
+//   hdr  : int32[64]  hdr[0] = 1 when it holds a set, [1] its nO,
+//                     [2] hits, [3] misses (calls that gathered)
+//   bits : uint32[ceil(K/32)]  the cached outlier bit set
+//   WO   : int8[N,K]  Wq[n, idx[i]] at column i < nO, zero pad to 16
+struct CacheLayout {
+    size_t hdr, bits, WO, total;
+};
+
+inline CacheLayout cache_layout(int64_t K, int64_t N)
+{
+    const size_t A = 256;
+    CacheLayout C;
+    size_t off = 0;
+    size_t nwords = (size_t)((K + 31) / 32);
+    C.hdr = off;  off = align_up(off + 256, A);
+    C.bits = off; off = align_up(off + 4 * (nwords ? nwords : 1), A);
+    C.WO = off;   off = align_up(off + (size_t)N * (size_t)K + 16, A);
+    C.total = off;
+    return C;
+}
+
 // Launchers (quant.hip).  All asynchronous on `s`; return hipGetLastError().
 hipError_t launch_quantize_weight(const uint16_t *W, int64_t N, int64_t K,
                                   int8_t *Wq, float *sW, hipStream_t s);
 // W16: null, or the fp16 weight [N,K] whose outlier columns are gathered
-// instead of those of Wq (the fp16-weight variant).
+// instead of those of Wq (the fp16-weight variant).  cache: null, or an
+// outlier-column cache (int8 path only) whose WO receives the gathered
+// columns, the gather being skipped when it already holds this call's set.
 hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W16,
                           uint16_t thr_mag, int64_t T, int64_t K, int64_t N, char *ws,
-                          const WsLayout &L, hipStream_t s);
+                          const WsLayout &L, hipStream_t s, char *cache = nullptr);
+hipError_t launch_cache_reset(char *cache, hipStream_t s);
 
 // Launcher (gemm.hip).
 // fp16w: the outlier product uses the fp16 weight columns that the prepare
 // call gathered from W16 (and the result is added after the scale sW).
+// WO: null (the workspace's gathered weight columns) or the cache's.
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K,
                        int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
-                       const WsLayout &L, bool fp16w, hipStream_t s);
+                       const WsLayout &L, bool fp16w, hipStream_t s,
+                       const int8_t *WO = nullptr);
 
 // Few-token path (decode.hip).  decode_shape(T, K) says whether both
 // entry points use it for this shape; the fused launch does the whole

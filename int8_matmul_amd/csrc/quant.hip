@@ -199,12 +199,13 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
     const uint16_t *__restrict__ W16, int T, int K, int N,
     int wrows, const uint32_t *__restrict__ bits_g, int32_t *__restrict__ meta,
     int32_t *__restrict__ idx_g, float *__restrict__ sX, int8_t *__restrict__ Xq,
-    uint16_t *__restrict__ XO, int8_t *__restrict__ WO)
+    uint16_t *__restrict__ XO, int8_t *__restrict__ WO, int32_t *__restrict__ cache_hdr,
+    uint32_t *__restrict__ cache_bits)
 {
     extern __shared__ uint32_t smem[];
     __shared__ int32_t scan[kThreads / 64];
     __shared__ uint32_t redr[ROWS][kThreads / 64];
-    __shared__ int nnz_s;
+    __shared__ int nnz_s, miss_s;
     constexpr int RREG = 4;   // chunks per thread and row kept in registers
     const int nw = (K + 31) / 32;
     uint32_t *bits = smem;
@@ -323,7 +324,25 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
         if (tid == 0)
             meta[0] = nO;
     }
-    if (nO == 0)
+    // Outlier-column cache (cache_hdr non-null): WO is the cache's copy of
+    // the gathered columns.  If the cache holds this call's exact set, the
+    // gather is skipped.  Every gather block decides alike (nothing writes
+    // the cached set during this kernel); k_cache_commit, the next kernel,
+    // records the set.
+    bool miss = true;
+    if (cache_hdr) {
+        if (tid == 0)
+            miss_s = cache_hdr[0] != 1;
+        __syncthreads();
+        bool diff = false;
+        for (int w = tid; w < nw; w += kThreads)
+            diff |= bits[w] != cache_bits[w];
+        if (diff)
+            atomicOr(&miss_s, 1);
+        __syncthreads();
+        miss = miss_s != 0;
+    }
+    if (!miss || nO == 0)   // nothing to gather
         return;
     // list the non-zero words once (one wave, ballot compaction), then
     // visit (row, non-zero word) pairs only
@@ -402,6 +421,47 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
     }
 }
 
+// After k_prepare on a cache: the same comparison as its gather blocks
+// (this call's bit set against the cached one), then the set is recorded
+// on a miss and the hit or miss counted.  One workgroup.
+__global__ __launch_bounds__(kThreads) void k_cache_commit(const uint32_t *__restrict__ bits,
+                                                           const int32_t *__restrict__ meta,
+                                                           int nw, int32_t *__restrict__ hdr,
+                                                           uint32_t *__restrict__ cbits)
+{
+    __shared__ int miss_s;
+    const int tid = threadIdx.x;
+    if (tid == 0)
+        miss_s = hdr[0] != 1;
+    __syncthreads();
+    bool diff = false;
+    for (int w = tid; w < nw; w += kThreads)
+        diff |= bits[w] != cbits[w];
+    if (diff)
+        atomicOr(&miss_s, 1);
+    __syncthreads();
+    const bool miss = miss_s != 0;
+    if (miss)
+        for (int w = tid; w < nw; w += kThreads)
+            cbits[w] = bits[w];
+    if (tid == 0) {
+        if (miss) {
+            hdr[1] = meta[0];
+            hdr[3] += 1;
+            hdr[0] = 1;
+        } else {
+            hdr[2] += 1;
+        }
+    }
+}
+
+// Marks an outlier-column cache empty (valid flag and counters zeroed).
+__global__ void k_cache_reset(int32_t *__restrict__ hdr)
+{
+    if (threadIdx.x < 64)
+        hdr[threadIdx.x] = 0;
+}
+
 } // namespace
 
 hipError_t launch_quantize_weight(const uint16_t *W, int64_t N, int64_t K, int8_t *Wq,
@@ -412,10 +472,18 @@ hipError_t launch_quantize_weight(const uint16_t *W, int64_t N, int64_t K, int8_
     return hipGetLastError();
 }
 
+hipError_t launch_cache_reset(char *cache, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_cache_reset, dim3(1), dim3(64), 0, s,
+                       reinterpret_cast<int32_t *>(cache + cache_layout(0, 0).hdr));
+    return hipGetLastError();
+}
+
 hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W16,
                           uint16_t thr_mag, int64_t T, int64_t K, int64_t N, char *ws,
-                          const WsLayout &L, hipStream_t s)
+                          const WsLayout &L, hipStream_t s, char *cache)
 {
+    const CacheLayout C = cache_layout(K, N);
     uint32_t *bits = reinterpret_cast<uint32_t *>(ws + L.bits);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + L.meta);
     const int nw = (int)((K + 31) / 32);
@@ -445,7 +513,13 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
                        reinterpret_cast<float *>(ws + L.sX),
                        reinterpret_cast<int8_t *>(ws + L.Xq),
                        reinterpret_cast<uint16_t *>(ws + L.XO),
-                       reinterpret_cast<int8_t *>(ws + L.WO));
+                       reinterpret_cast<int8_t *>(cache ? cache + C.WO : ws + L.WO),
+                       cache ? reinterpret_cast<int32_t *>(cache + C.hdr) : nullptr,
+                       cache ? reinterpret_cast<uint32_t *>(cache + C.bits) : nullptr);
+    if (cache)
+        hipLaunchKernelGGL(k_cache_commit, dim3(1), dim3(kThreads), 0, s, bits, meta, nw,
+                           reinterpret_cast<int32_t *>(cache + C.hdr),
+                           reinterpret_cast<uint32_t *>(cache + C.bits));
     return hipGetLastError();
 }
 

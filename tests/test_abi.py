@@ -44,6 +44,8 @@ def test_header_declares_the_expected_entry_points():
         "llm_int8_linear_fp16w", "llm_int8_prepare_fp16w", "llm_int8_gemm_fp16w",
         "smoothquant_column_absmax", "smoothquant_factors", "smoothquant_quantize_weight",
         "smoothquant_prepare", "smoothquant_linear",
+        "llm_int8_cache_bytes", "llm_int8_cache_reset", "llm_int8_linear_cached",
+        "llm_int8_prepare_cached", "llm_int8_gemm_cached",
     ])
 
 
@@ -190,6 +192,29 @@ def test_smoothquant_validation(lib):
     assert L(P, P, MIS, P, 32, 64, 48, P2, P, need, None) == ALIGN
     assert L(P, P, P, P, 32, 65, 48, P2, P, need, None) == SHAPE
     assert L(None, None, None, None, 32, 64, 0, None, None, 0, None) == OK
+
+
+def test_cache_validation(lib):
+    assert lib.llm_int8_cache_bytes(72, 48) == 0            # K % 16
+    cb = lib.llm_int8_cache_bytes(64, 48)
+    assert cb >= 64 * 48 + 256
+    r = lib.llm_int8_cache_reset
+    assert r(None, cb, 64, 48, None) == INVALID
+    assert r(MIS, cb, 64, 48, None) == ALIGN
+    assert r(P, cb - 1, 64, 48, None) == WORKSPACE
+    need = lib.llm_int8_workspace_bytes(32, 64, 48)
+    L = lib.llm_int8_linear_cached
+    assert L(P, P, P, 6.0, 32, 64, 48, P2, P, need, None, cb, None) == INVALID
+    assert L(P, P, P, 6.0, 32, 64, 48, P2, P, need, MIS, cb, None) == ALIGN
+    assert L(P, P, P, 6.0, 32, 64, 48, P2, P, need, P2, cb - 1, None) == WORKSPACE
+    assert L(P, P, P, math.nan, 32, 64, 48, P2, P, need, P2, cb, None) == INVALID
+    assert L(None, None, None, 6.0, 0, 64, 48, None, None, 0, None, 0, None) == OK
+    p = lib.llm_int8_prepare_cached
+    assert p(P, P, 6.0, 32, 64, 48, P, need, None, cb, None) == INVALID
+    assert p(P, P, 6.0, 32, 64, 48, P, need, P2, 0, None) == WORKSPACE
+    g = lib.llm_int8_gemm_cached
+    assert g(P, P, 32, 64, 48, P2, None, P, need, None, cb, None) == INVALID
+    assert g(P, P, 32, 64, 48, P2, None, P, need, MIS, cb, None) == ALIGN
 
 
 def test_python_binding_rejects_cpu_tensors(lib):
