@@ -51,6 +51,9 @@ def parse():
                          "alpha 0.5, calibrated on the first 512 rows of X); cached: "
                          "llm_int8_linear_cached with an outlier-column cache (every call "
                          "after the first reuses the gathered weight columns)")
+    ap.add_argument("--cold", action="store_true",
+                    help="rotate copies of the call's buffers (more than 2 x 256 MB per cycle) "
+                         "so that no call finds its operands in the Infinity Cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables it)")
     ap.add_argument("--no-reference", action="store_true",
@@ -142,92 +145,115 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     X_np, W_np, _ = workloads.make(args.workload)
-    X = torch.from_numpy(X_np).to(dev)
-    W = torch.from_numpy(W_np).to(dev)
-    Wq, sW = li8.quantize_weight(W)
-    ws = li8.new_workspace(T, K, N, dev)
-    Y = torch.empty((T, N), dtype=torch.float16, device=dev)
-    torch.cuda.synchronize()
-
+    X0 = torch.from_numpy(X_np).to(dev)
+    W0 = torch.from_numpy(W_np).to(dev)
+    s_inv = None
     if args.variant == "sq":
         # offline, once per layer: factors from a calibration batch (the first
         # 512 token rows) and the weight's column maxima; smoothed weight codes
-        ax = li8.smoothquant_column_absmax(X[:512])
-        s_f, s_inv = li8.smoothquant_factors(ax, li8.smoothquant_column_absmax(W), 0.5)
-        Wq, sW = li8.smoothquant_quantize_weight(W, s_f)
-        torch.cuda.synchronize()
-
-        def call():
-            li8.smoothquant_linear(X, s_inv, Wq, sW, out=Y, workspace=ws)
-
-        def prep():
-            li8.smoothquant_prepare(X, s_inv, N, ws)
-
-        def gemm():
-            li8.gemm(Wq, sW, T, ws, out=Y)
-    elif args.variant == "cached":
-        cache = li8.new_cache(K, N, dev)
-
-        def call():
-            li8.linear_cached(X, Wq, sW, cache, thr, out=Y, workspace=ws)
-
-        def prep():
-            li8.prepare_cached(X, Wq, thr, ws, cache)
-
-        def gemm():
-            li8.gemm_cached(Wq, sW, T, ws, cache, out=Y)
-    elif args.variant == "fp16w":
-        def call():
-            li8.linear_fp16w(X, Wq, sW, W, thr, out=Y, workspace=ws)
-
-        def prep():
-            li8.prepare_fp16w(X, W, thr, ws)
-
-        def gemm():
-            li8.gemm_fp16w(Wq, sW, W, T, ws, out=Y)
+        ax = li8.smoothquant_column_absmax(X0[:512])
+        s_f, s_inv = li8.smoothquant_factors(ax, li8.smoothquant_column_absmax(W0), 0.5)
+        Wq0, sW0 = li8.smoothquant_quantize_weight(W0, s_f)
     else:
-        def call():
-            li8.linear(X, Wq, sW, thr, out=Y, workspace=ws)
+        Wq0, sW0 = li8.quantize_weight(W0)
 
-        def prep():
-            li8.prepare(X, Wq, thr, ws)
+    # Buffer sets: one (warm: the call's operands stay in the caches between
+    # calls), or with --cold enough copies that the calls of a cycle touch
+    # more than twice the 256 MB Infinity Cache, so every call reads its
+    # weight and activations from HBM.
+    touched = 2 * T * K + N * K + 2 * T * N + T * K + 4 * (T + N)
+    nsets = max(2, -(-2 * 256 * 2**20 // touched)) if args.cold else 1
 
-        def gemm():
-            li8.gemm(Wq, sW, T, ws, out=Y)
+    def new_set(first):
+        st_ = dict(X=X0 if first else X0.clone(), Wq=Wq0 if first else Wq0.clone(),
+                   sW=sW0 if first else sW0.clone(),
+                   ws=li8.new_workspace(T, K, N, dev),
+                   Y=torch.empty((T, N), dtype=torch.float16, device=dev))
+        if args.variant == "fp16w":
+            st_["W"] = W0 if first else W0.clone()
+        if args.variant == "cached":
+            st_["cache"] = li8.new_cache(K, N, dev)
+        return st_
 
-    for _ in range(args.warmup):
-        call()
+    sets = [new_set(i == 0) for i in range(nsets)]
+    X, W, Wq, sW, ws, Y = X0, W0, Wq0, sW0, sets[0]["ws"], sets[0]["Y"]
+    torch.cuda.synchronize()
+
+    if args.variant == "sq":
+        def call(b):
+            li8.smoothquant_linear(b["X"], s_inv, b["Wq"], b["sW"], out=b["Y"], workspace=b["ws"])
+
+        def prep(b):
+            li8.smoothquant_prepare(b["X"], s_inv, N, b["ws"])
+
+        def gemm(b):
+            li8.gemm(b["Wq"], b["sW"], T, b["ws"], out=b["Y"])
+    elif args.variant == "cached":
+        def call(b):
+            li8.linear_cached(b["X"], b["Wq"], b["sW"], b["cache"], thr, out=b["Y"],
+                              workspace=b["ws"])
+
+        def prep(b):
+            li8.prepare_cached(b["X"], b["Wq"], thr, b["ws"], b["cache"])
+
+        def gemm(b):
+            li8.gemm_cached(b["Wq"], b["sW"], T, b["ws"], b["cache"], out=b["Y"])
+    elif args.variant == "fp16w":
+        def call(b):
+            li8.linear_fp16w(b["X"], b["Wq"], b["sW"], b["W"], thr, out=b["Y"], workspace=b["ws"])
+
+        def prep(b):
+            li8.prepare_fp16w(b["X"], b["W"], thr, b["ws"])
+
+        def gemm(b):
+            li8.gemm_fp16w(b["Wq"], b["sW"], b["W"], T, b["ws"], out=b["Y"])
+    else:
+        def call(b):
+            li8.linear(b["X"], b["Wq"], b["sW"], thr, out=b["Y"], workspace=b["ws"])
+
+        def prep(b):
+            li8.prepare(b["X"], b["Wq"], thr, b["ws"])
+
+        def gemm(b):
+            li8.gemm(b["Wq"], b["sW"], T, b["ws"], out=b["Y"])
+
+    for i in range(max(args.warmup, nsets)):
+        call(sets[i % nsets])
     torch.cuda.synchronize()
     y_eager = Y.clone()
 
     def capture(fn, reps):
-        """A HIP graph of `reps` back-to-back calls of fn (no allocation inside)."""
+        """A HIP graph of `reps` back-to-back calls of fn, cycling over the
+        buffer sets (no allocation inside)."""
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            fn()
+            fn(sets[0])
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _ in range(reps):
-                fn()
+            for r in range(reps):
+                fn(sets[r % nsets])
         torch.cuda.synchronize()
         return g
 
     def same_as_eager(what):
-        if not torch.equal(Y.view(torch.int16), y_eager.view(torch.int16)):
-            raise RuntimeError(f"{what}: graph replay differs from the eager call")
+        for b in sets:
+            if not torch.equal(b["Y"].view(torch.int16), y_eager.view(torch.int16)):
+                raise RuntimeError(f"{what}: graph replay differs from the eager call")
 
     # The K timed steps are one HIP graph of K calls of the product entry
     # point, so that the host's per-call launch cost (Python, ctypes) does
     # not pace a short call; the graph's output is checked against the eager
     # call before and after timing.
     g_lin = capture(call, args.steps)
-    Y.zero_()
+    for b in sets:
+        b["Y"].zero_()
     g_lin.replay()
     torch.cuda.synchronize()
-    same_as_eager("linear")
+    if args.steps >= nsets:
+        same_as_eager("linear")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -236,7 +262,8 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    same_as_eager("linear (timed)")
+    if args.steps >= nsets:
+        same_as_eager("linear (timed)")
     ms_step = (t1 - t0) * 1e3 / args.steps
     gpu_ms_step = e0.elapsed_time(e1) / args.steps
 
@@ -261,7 +288,8 @@ def main():
         return a.elapsed_time(b) / R
 
     if few:
-        prep()   # (the fused call leaves the workspace unwritten)
+        for b in sets:   # (the fused call leaves the workspaces unwritten)
+            prep(b)
         g_gemm = capture(gemm, R)
         gemm_ms = graph_ms(g_gemm)
         del g_gemm
@@ -269,13 +297,14 @@ def main():
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(R)]
         torch.cuda.synchronize()
         for i in range(R):
-            prep()
+            prep(sets[i % nsets])
             ev[i][0].record()
-            gemm()
+            gemm(sets[i % nsets])
             ev[i][1].record()
         torch.cuda.synchronize()
         gemm_ms = sum(a.elapsed_time(b) for a, b in ev) / R
-    same_as_eager("prepare + gemm")
+    if R >= nsets:
+        same_as_eager("prepare + gemm")
     g_prep = capture(prep, R)
     prep_ms = graph_ms(g_prep)
     del g_lin, g_prep
@@ -385,7 +414,10 @@ def main():
                    "outlier_cache": args.variant == "cached",
                    "method": ("SmoothQuant-style W8A8, alpha 0.5" if args.variant == "sq"
                               else "LLM.int8() decomposition"),
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "cache_state": (f"cold: {nsets} rotating copies of the call's buffers, "
+                                   f"{nsets * touched / 1e6:.0f} MB touched per cycle"
+                                   if args.cold else "warm: one buffer set")},
         "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
         "path": ("few-token fused kernel" if few and args.variant != "sq" else
                  "prepare kernel + few-token GEMM" if few else "prepare kernels + tiled GEMM"),
