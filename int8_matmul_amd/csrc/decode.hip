@@ -110,7 +110,9 @@ __device__ void outlier_columns8(const uint32_t *bits, const int32_t *pre, int n
     }
 }
 
-template <bool FUSED, int KB, bool F16W, bool STORE_ACC>
+// TB: a compile-time bound on T (8 or 16), so that the per-token loops of
+// the activation work run over T <= 8 slots when that suffices.
+template <bool FUSED, int KB, int TB, bool F16W, bool STORE_ACC>
 __global__ __launch_bounds__(kDThreads) void k_decode(
     const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq, const float *__restrict__ sW,
     const uint16_t *__restrict__ W16,
@@ -157,21 +159,22 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     // The activation loads are issued before the first weight batch: loads
     // complete in order, so this way the activation work waits only for
     // its own data while the weight batch is in flight.  (The fused
-    // variant with two chunks of X per thread has no registers to spare
-    // for the weights during that work: it requests them after it.)
-    constexpr bool kEarly = !(FUSED && KB > 8);
+    // variant with two chunks of X per thread for 16 token slots has no
+    // registers to spare for the weights during that work: it requests
+    // them after it.)
+    constexpr bool kEarly = !(FUSED && KB > 8 && TB > 8);
     int nO;
     if constexpr (FUSED) {
         constexpr int CPT = KB / 8;   // 8-column chunks per thread: K <= 4096*CPT
         const int nchunk = K / 8;
         const int nw = (K + 31) / 32;
         const uint4 *x4 = reinterpret_cast<const uint4 *>(X);
-        uint4 xv[CPT][kDMaxT];
+        uint4 xv[CPT][TB];
 #pragma unroll
         for (int u = 0; u < CPT; u++) {
             const int c = tid + u * kDThreads;
 #pragma unroll
-            for (int t = 0; t < kDMaxT; t++) {
+            for (int t = 0; t < TB; t++) {
                 xv[u][t] = make_uint4(0, 0, 0, 0);
                 if (t < T && c < nchunk)
                     xv[u][t] = x4[(int64_t)t * (K / 8) + c];
@@ -180,16 +183,16 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         if (kEarly && rg < NRG)
             wload(0, rg);
         uint32_t fl[CPT];
-        uint32_t rm[kDMaxT];
+        uint32_t rm[TB];
 #pragma unroll
-        for (int t = 0; t < kDMaxT; t++)
+        for (int t = 0; t < TB; t++)
             rm[t] = 0;
 #pragma unroll
         for (int u = 0; u < CPT; u++) {
             const int c = tid + u * kDThreads;
             li8_us2 mx[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
 #pragma unroll
-            for (int t = 0; t < kDMaxT; t++)
+            for (int t = 0; t < TB; t++)
                 column_max8(mx, xv[u][t]);   // padding rows are zero
             fl[u] = outlier_flags8(mx, thr_mag);
             // chunks 4w..4w+3 sit in four consecutive lanes: one word
@@ -199,18 +202,18 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             if ((c & 3) == 0 && c < nchunk)
                 bits[c >> 2] = word;
 #pragma unroll
-            for (int t = 0; t < kDMaxT; t++)
+            for (int t = 0; t < TB; t++)
                 rm[t] = max(rm[t], chunk_max(xv[u][t], fl[u]));
         }
         // all reductions first (they overlap), then the stores
-        uint32_t wm[kDMaxT];
+        uint32_t wm[TB];
 #pragma unroll
-        for (int t = 0; t < kDMaxT; t++)
+        for (int t = 0; t < TB; t++)
             wm[t] = wave_max(rm[t]);
-        if (lane < kDMaxT) {
+        if (lane < TB) {
             uint32_t m = wm[0];
 #pragma unroll
-            for (int t = 1; t < kDMaxT; t++)
+            for (int t = 1; t < TB; t++)
                 m = (lane == t) ? wm[t] : m;
             rmax[wid * kDMaxT + lane] = m;
         }
@@ -221,15 +224,15 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             uint32_t m = 0;
 #pragma unroll
             for (int w = 0; w < kDWaves; w++)
-                m = max(m, rmax[w * kDMaxT + tid]);
+                m = max(m, tid < TB ? rmax[w * kDMaxT + tid] : 0u);
             const float sc = h2f(m) / 127.0f;
             sxl[tid] = sc;
             rxl[tid] = 1.0f / sc;
         }
         lds_barrier();
-        float sx[kDMaxT], rx[kDMaxT];
+        float sx[TB], rx[TB];
 #pragma unroll
-        for (int t = 0; t < kDMaxT; t++) {
+        for (int t = 0; t < TB; t++) {
             sx[t] = sxl[t];
             rx[t] = rxl[t];
         }
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             const int c = tid + u * kDThreads;
             if (c < nchunk) {
 #pragma unroll
-                for (int t = 0; t < kDMaxT; t++)
+                for (int t = 0; t < TB; t++)
                     if (t < T) {
                         const uint2 q = (sx[t] == 0.0f) ? make_uint2(0u, 0u)
                                                         : token_codes8(xv[u][t], fl[u], sx[t], rx[t]);
@@ -286,9 +289,9 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // contract) gives wrong values, not reads out of bounds
         nO = min(max(meta[0], 0), K);
         const int nq = K / 16, tot = T * nq;
-        uint4 st[kDMaxT];
+        uint4 st[TB];
 #pragma unroll
-        for (int j = 0; j < kDMaxT; j++) {
+        for (int j = 0; j < TB; j++) {
             const int i = tid + j * kDThreads;
             if (i < tot) {
                 const int t = i / nq, q = i - t * nq;
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         if (rg < NRG)
             wload(0, rg);
 #pragma unroll
-        for (int j = 0; j < kDMaxT; j++) {
+        for (int j = 0; j < TB; j++) {
             const int i = tid + j * kDThreads;
             if (i < tot) {
                 const int t = i / nq, q = i - t * nq;
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     }
 }
 
-template <bool FUSED, int KB, bool F16W>
+template <bool FUSED, int KB, int TB, bool F16W>
 hipError_t launch_kb(const uint16_t *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
                      uint32_t thr_mag,
                      int64_t T, int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
@@ -481,10 +484,10 @@ hipError_t launch_kb(const uint16_t *X, const int8_t *Wq, const float *sW, const
     const int8_t *Xq = FUSED ? nullptr : reinterpret_cast<const int8_t *>(ws + L.Xq);
     const uint16_t *XO = FUSED ? nullptr : reinterpret_cast<const uint16_t *>(ws + L.XO);
     if (acc)
-        hipLaunchKernelGGL((k_decode<FUSED, KB, F16W, true>), grid, dim3(kDThreads), 0, s, X, Wq,
+        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, true>), grid, dim3(kDThreads), 0, s, X, Wq,
                            sW, W16, thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
     else
-        hipLaunchKernelGGL((k_decode<FUSED, KB, F16W, false>), grid, dim3(kDThreads), 0, s, X, Wq,
+        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, false>), grid, dim3(kDThreads), 0, s, X, Wq,
                            sW, W16, thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
     return hipGetLastError();
 }
@@ -496,18 +499,27 @@ bool decode_shape(int64_t T, int64_t K)
     return T >= 1 && T <= kDecodeMaxT && K >= 16 && K <= kDecodeMaxK;
 }
 
+// KB (weight 16-byte loads per lane and row group) by K, TB by T.
+template <bool FUSED, bool F16W>
+hipError_t launch_decode(const uint16_t *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
+                         uint32_t thr_mag, int64_t T, int64_t K, int64_t N, uint16_t *Y,
+                         int32_t *acc, const char *ws, const WsLayout &L, hipStream_t s)
+{
+    if (K <= 4096)
+        return T <= 8 ? launch_kb<FUSED, 8, 8, F16W>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc, ws, L, s)
+                      : launch_kb<FUSED, 8, 16, F16W>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc, ws, L, s);
+    return T <= 8 ? launch_kb<FUSED, 16, 8, F16W>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc, ws, L, s)
+                  : launch_kb<FUSED, 16, 16, F16W>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc, ws, L, s);
+}
+
 hipError_t launch_decode_fused(const uint16_t *X, const int8_t *Wq, const float *sW,
                                const uint16_t *W16, uint16_t thr_mag, int64_t T, int64_t K,
                                int64_t N, uint16_t *Y, hipStream_t s)
 {
     static const WsLayout none{};
     if (W16)
-        return K <= 4096
-                   ? launch_kb<true, 8, true>(X, Wq, sW, W16, thr_mag, T, K, N, Y, nullptr, nullptr, none, s)
-                   : launch_kb<true, 16, true>(X, Wq, sW, W16, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
-    return K <= 4096
-               ? launch_kb<true, 8, false>(X, Wq, sW, nullptr, thr_mag, T, K, N, Y, nullptr, nullptr, none, s)
-               : launch_kb<true, 16, false>(X, Wq, sW, nullptr, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
+        return launch_decode<true, true>(X, Wq, sW, W16, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
+    return launch_decode<true, false>(X, Wq, sW, nullptr, thr_mag, T, K, N, Y, nullptr, nullptr, none, s);
 }
 
 hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, const uint16_t *W16, int64_t T,
@@ -515,10 +527,8 @@ hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, const uint16_t 
                               const WsLayout &L, hipStream_t s)
 {
     if (W16)
-        return K <= 4096 ? launch_kb<false, 8, true>(nullptr, Wq, sW, W16, 0, T, K, N, Y, acc, ws, L, s)
-                         : launch_kb<false, 16, true>(nullptr, Wq, sW, W16, 0, T, K, N, Y, acc, ws, L, s);
-    return K <= 4096 ? launch_kb<false, 8, false>(nullptr, Wq, sW, nullptr, 0, T, K, N, Y, acc, ws, L, s)
-                     : launch_kb<false, 16, false>(nullptr, Wq, sW, nullptr, 0, T, K, N, Y, acc, ws, L, s);
+        return launch_decode<false, true>(nullptr, Wq, sW, W16, 0, T, K, N, Y, acc, ws, L, s);
+    return launch_decode<false, false>(nullptr, Wq, sW, nullptr, 0, T, K, N, Y, acc, ws, L, s);
 }
 
 } // namespace li8

@@ -153,6 +153,8 @@ def test_ragged_shapes(T, K, N, thr):
     (16, 8192, 130),     # the largest few-token shape
     (15, 1024, 1),       # a single output feature
     (16, 16, 33),        # one 16-column block of K
+    (9, 2048, 100),      # the first T past the 8-token bound
+    (8, 8192, 70),       # 8 tokens, two chunks of X per thread, the largest K
 ])
 @pytest.mark.parametrize("thr", [6.0, np.inf, 0.0])
 def test_decode_shapes(T, K, N, thr):
