@@ -144,13 +144,21 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     const int tok = lane & 15;    // token slot (B column) of this lane
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wq, N * K);
 
+    // Every load below is unconditional, with an out-of-range offset (zeros)
+    // where a lane has nothing to read, and the test is per lane: loads
+    // behind branches leave the compiler unable to count the loads in
+    // flight, and it then waits for all of them (weights included) before
+    // the first use of any.
     v4i wbuf[2][KB];
+    const int kend = min(s1 * 64, K);   // end of this wave's share of K
+    // (a row group past the last one, rg >= NRG, reads zeros)
     auto wload = [&](int set, int rg) {
         const int n = min(rg * kDRows + (lane & 15), N - 1);
+        const int kl = rg < NRG ? kend : 0;
 #pragma unroll
         for (int j = 0; j < KB; j++) {
             const int k = (s0 + j) * 64 + 16 * kg;
-            wbuf[set][j] = load_w16(rW, (s0 + j < s1 && k < K) ? n * K + k : kOutOfRange);
+            wbuf[set][j] = load_w16(rW, k < kl ? n * K + k : kOutOfRange);
         }
     };
     int rg = blockIdx.x;
@@ -168,19 +176,18 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         constexpr int CPT = KB / 8;   // 8-column chunks per thread: K <= 4096*CPT
         const int nchunk = K / 8;
         const int nw = (K + 31) / 32;
-        const uint4 *x4 = reinterpret_cast<const uint4 *>(X);
+        const __amdgpu_buffer_rsrc_t rX = make_rsrc(X, 2 * T * K);
         uint4 xv[CPT][TB];
 #pragma unroll
         for (int u = 0; u < CPT; u++) {
             const int c = tid + u * kDThreads;
 #pragma unroll
-            for (int t = 0; t < TB; t++) {
-                xv[u][t] = make_uint4(0, 0, 0, 0);
-                if (t < T && c < nchunk)
-                    xv[u][t] = x4[(int64_t)t * (K / 8) + c];
+            for (int t = 0; t < TB; t++) {   // rows past T and chunks past K read zeros
+                const bool ok = (t < T) & (c < nchunk);
+                xv[u][t] = __builtin_bit_cast(uint4, load_w16(rX, ok ? 16 * (t * (K / 8) + c) : kOutOfRange));
             }
         }
-        if (kEarly && rg < NRG)
+        if constexpr (kEarly)   // (rg = blockIdx.x < NRG: the grid is at most NRG)
             wload(0, rg);
         uint32_t fl[CPT];
         uint32_t rm[TB];
@@ -289,17 +296,19 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // contract) gives wrong values, not reads out of bounds
         nO = min(max(meta[0], 0), K);
         const int nq = K / 16, tot = T * nq;
+        const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Xq_g, T * K);
+        const __amdgpu_buffer_rsrc_t rS = make_rsrc(sX_g, 4 * T);
         uint4 st[TB];
 #pragma unroll
-        for (int j = 0; j < TB; j++) {
+        for (int j = 0; j < TB; j++) {   // (row-major [T,K]: chunk i is at byte 16 i)
             const int i = tid + j * kDThreads;
-            if (i < tot) {
-                const int t = i / nq, q = i - t * nq;
-                st[j] = *reinterpret_cast<const uint4 *>(Xq_g + (int64_t)t * K + 16 * q);
-            }
+            st[j] = __builtin_bit_cast(uint4, load_w16(rQ, i < tot ? 16 * i : kOutOfRange));
         }
-        if (rg < NRG)
-            wload(0, rg);
+        // the token scales too before the weights: loads complete in order,
+        // so a later load would wait for the whole weight batch
+        const float sxg = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rS, tid < T ? 4 * tid : kOutOfRange, 0, 0));
+        wload(0, rg);
 #pragma unroll
         for (int j = 0; j < TB; j++) {
             const int i = tid + j * kDThreads;
@@ -309,11 +318,11 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             }
         }
         if (tid < kDMaxT)
-            sxl[tid] = tid < T ? sX_g[tid] : 0.0f;
+            sxl[tid] = sxg;
         lds_barrier();
     }
 
-    if (!kEarly && rg < NRG)
+    if constexpr (!kEarly)
         wload(0, rg);
 
     // ---- row groups: int8 MFMAs over this wave's share of K ----
@@ -457,14 +466,12 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     // are issued before this group's MFMAs
     while (rg < NRG) {
         const int rg1 = rg + G;
-        if (rg1 < NRG)
-            wload(1, rg1);
+        wload(1, rg1);   // zeros past the last group
         process(0, rg, 0);
         if (rg1 >= NRG)
             break;
         const int rg2 = rg1 + G;
-        if (rg2 < NRG)
-            wload(0, rg2);
+        wload(0, rg2);
         process(1, rg1, 1);
         rg = rg2;
     }
