@@ -144,19 +144,39 @@ __global__ __launch_bounds__(kThreads) void k_detect(
         atomicOr(bits + (c >> 2), word);
 }
 
+// Bit-set words held in registers per thread by k_prepare (nw <= 256,
+// i.e. K <= 8192); longer bit sets are read from global memory.
+constexpr int kBitsPerThread = 1;
+
 // Load the bit set into LDS and write the exclusive prefix of the
-// popcounts per word; returns nO (the total) to every thread.
+// popcounts per word; returns nO (the total) to every thread.  Thread tid
+// owns words [tid*per, tid*per + per); with REG, bw already holds them
+// (nw <= kBitsPerThread * kThreads).
+template <bool REG>
 __device__ int load_bits_and_scan(const uint32_t *__restrict__ bits_g, int nw,
-                                  uint32_t *bits, int32_t *pre, int32_t *scan)
+                                  uint32_t *bits, int32_t *pre, int32_t *scan,
+                                  const uint32_t (&bw)[kBitsPerThread])
 {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int per = (nw + kThreads - 1) / kThreads;
     const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
     int s = 0;
-    for (int w = w0; w < w1; w++) {
-        uint32_t b = bits_g[w];
-        bits[w] = b;
-        s += __popc(b);
+    if constexpr (REG) {
+        // (a select, not a branch, consumes bw: a load whose only use sits
+        // in a branch is moved into it, behind the row loads)
+#pragma unroll
+        for (int i = 0; i < kBitsPerThread; i++) {
+            const uint32_t b = (w0 + i < w1) ? bw[i] : 0u;
+            s += __popc(b);
+            if (w0 + i < w1)
+                bits[w0 + i] = b;
+        }
+    } else {
+        for (int w = w0; w < w1; w++) {
+            uint32_t b = bits_g[w];
+            bits[w] = b;
+            s += __popc(b);
+        }
     }
     // inclusive scan within the wave
     int v = s;
@@ -193,7 +213,8 @@ __device__ int load_bits_and_scan(const uint32_t *__restrict__ bits_g, int nw,
 // gives each outlier column its compact index.
 // ---------------------------------------------------------------------------
 
-template <int ROWS>
+// REG: the bit set fits in kBitsPerThread words per thread (K <= 8192).
+template <int ROWS, bool REG>
 __global__ __launch_bounds__(kThreads) void k_prepare(
     const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq,
     const uint16_t *__restrict__ W16, int T, int K, int N,
@@ -216,22 +237,39 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
     const bool xblock = (int)blockIdx.x < xblocks;
     const int t0 = blockIdx.x * ROWS;
 
-    // token rows: issue every load before the bit-set scan so that both
-    // latencies overlap
+    // Loads first, all unconditional: this thread's bit-set words, then the
+    // token rows (buffer loads; chunks past the row and the lanes of
+    // weight-gather blocks use offset 2^31, past the buffer whenever X is
+    // under 2 GiB, else a valid address whose value is not used).  Loads behind branches would make the compiler wait for all
+    // of them at the first use; this way the bit-set scan waits only for
+    // the bit-set words (loads complete in order) while the rows arrive.
+    uint32_t bw[kBitsPerThread] = {};
+    if constexpr (REG) {
+        const int per = (nw + kThreads - 1) / kThreads;
+        const int w0 = tid * per, wl = nw > 0 ? nw - 1 : 0;   // (the region has >= 1 word)
+#pragma unroll
+        for (int i = 0; i < kBitsPerThread; i++)
+            bw[i] = bits_g[min(w0 + i, wl)];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // (keep the row loads after them)
     uint4 v[ROWS][RREG];
-    if (xblock) {
+    {
+        const __amdgpu_buffer_rsrc_t rX =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(X), (short)0,
+                                              (int)(2u * (unsigned)T * (unsigned)K), 0x00020000);
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
-            const uint4 *xr = reinterpret_cast<const uint4 *>(X + (int64_t)min(t0 + r, T - 1) * K);
+            const unsigned row = (unsigned)min(t0 + r, T - 1);
 #pragma unroll
             for (int s = 0; s < RREG; s++) {
                 const int c = tid + s * kThreads;
-                if (c < nchunk)
-                    v[r][s] = xr[c];
+                const int off = (xblock & (c < nchunk)) ? (int)(16u * (row * (unsigned)nchunk + (unsigned)c))
+                                                        : (int)0x80000000;
+                v[r][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
             }
         }
     }
-    const int nO = load_bits_and_scan(bits_g, nw, bits, pre, scan);
+    const int nO = load_bits_and_scan<REG>(bits_g, nw, bits, pre, scan, bw);
     const int nO16 = (nO + 15) & ~15;   // <= K since K % 16 == 0
 
     if (xblock) {
@@ -507,7 +545,9 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
     const int64_t wblocks = (N + wrows - 1) / wrows;
     const size_t lds = 12 * (size_t)(nw > 0 ? nw : 1);   // bits, prefix, non-zero words
     const int64_t xblocks = (T + kPrepRows - 1) / kPrepRows;
-    hipLaunchKernelGGL(k_prepare<kPrepRows>, dim3((unsigned)(xblocks + wblocks)), dim3(kThreads), lds, s, X, Wq,
+    auto kp = nw <= kBitsPerThread * kThreads ? k_prepare<kPrepRows, true> : k_prepare<kPrepRows, false>;
+    auto launch = [&](auto KP) {
+    hipLaunchKernelGGL(KP, dim3((unsigned)(xblocks + wblocks)), dim3(kThreads), lds, s, X, Wq,
                        W16, (int)T, (int)K, (int)N, wrows, bits, meta,
                        reinterpret_cast<int32_t *>(ws + L.idx),
                        reinterpret_cast<float *>(ws + L.sX),
@@ -516,6 +556,8 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
                        reinterpret_cast<int8_t *>(cache ? cache + C.WO : ws + L.WO),
                        cache ? reinterpret_cast<int32_t *>(cache + C.hdr) : nullptr,
                        cache ? reinterpret_cast<uint32_t *>(cache + C.bits) : nullptr);
+    };
+    launch(kp);
     if (cache)
         hipLaunchKernelGGL(k_cache_commit, dim3(1), dim3(kThreads), 0, s, bits, meta, nw,
                            reinterpret_cast<int32_t *>(cache + C.hdr),

@@ -120,8 +120,9 @@ __global__ __launch_bounds__(kSThreads) void k_sq_quantize_weight(
 // Writes Xq (codes of X * r), sX, and meta[0] = 0 outlier columns (block 0)
 // for the GEMM.  The smoothed row is kept in registers between the absmax
 // pass and the code pass for K <= 8 * 256 * kSq; longer rows are re-read.
-constexpr int kSq = 4;   // 8-column chunks per thread held in registers
-
+// kSq (8-column chunks per thread held in registers) is chosen from K at
+// launch, so that no thread issues loads for chunks past the row.
+template <int kSq>
 __global__ __launch_bounds__(kSThreads) void k_sq_rows(const uint16_t *__restrict__ X,
                                                        const float *__restrict__ r, int K,
                                                        int8_t *__restrict__ Xq,
@@ -135,6 +136,11 @@ __global__ __launch_bounds__(kSThreads) void k_sq_rows(const uint16_t *__restric
     const float4 *r4 = reinterpret_cast<const float4 *>(r);
     if (t == 0 && threadIdx.x == 0)
         meta[0] = 0;
+    if (nchunk == 0) {   // K = 0: an empty row
+        if (threadIdx.x == 0)
+            sX[t] = 0.0f;
+        return;
+    }
     auto smooth = [&](int c, float v[8]) {
         const uint4 x = xr[c];
         const float4 ra = r4[2 * c], rb = r4[2 * c + 1];
@@ -144,18 +150,21 @@ __global__ __launch_bounds__(kSThreads) void k_sq_rows(const uint16_t *__restric
         for (int e = 0; e < 8; e++)
             v[e] = h2f_sq((w[e >> 1] >> (16 * (e & 1))) & 0xffffu) * rr[e];
     };
+    // the register-held chunks are loaded unconditionally (a chunk past
+    // the row re-reads the last one and is not used), so that all loads are
+    // in flight together: loads behind branches make the compiler wait for
+    // each before the next
     float v[kSq][8];
     float a = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kSq; u++) {
-        const int c = threadIdx.x + u * kSThreads;
-        if (c < nchunk) {
-            smooth(c, v[u]);
+    for (int u = 0; u < kSq; u++)
+        smooth(min((int)threadIdx.x + u * kSThreads, nchunk - 1), v[u]);
+#pragma unroll
+    for (int u = 0; u < kSq; u++)
+        if ((int)threadIdx.x + u * kSThreads < nchunk)
 #pragma unroll
             for (int e = 0; e < 8; e++)
                 a = fmaxf(a, fabsf(v[u][e]));
-        }
-    }
     for (int c = threadIdx.x + kSq * kSThreads; c < nchunk; c += kSThreads) {
         float w8[8];
         smooth(c, w8);
@@ -232,7 +241,9 @@ hipError_t launch_sq_quantize_weight(const uint16_t *W, const float *sf, int64_t
 hipError_t launch_sq_prepare(const uint16_t *X, const float *r, int64_t T, int64_t K, char *ws,
                              const WsLayout &L, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_sq_rows, dim3((unsigned)T), dim3(kSThreads), 0, s, X, r, (int)K,
+    const int64_t need = (K / 8 + kSThreads - 1) / kSThreads;   // chunks per thread
+    auto kern = need <= 1 ? k_sq_rows<1> : need <= 2 ? k_sq_rows<2> : k_sq_rows<4>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)T), dim3(kSThreads), 0, s, X, r, (int)K,
                        reinterpret_cast<int8_t *>(ws + L.Xq), reinterpret_cast<float *>(ws + L.sX),
                        reinterpret_cast<int32_t *>(ws + L.meta));
     return hipGetLastError();
