@@ -121,6 +121,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     const float *__restrict__ sX_g, const int8_t *__restrict__ Xq_g,
     const uint16_t *__restrict__ XO_g, uint16_t *__restrict__ Y, int32_t *__restrict__ acc_out)
 {
+    static_assert(KB % 8 == 0, "weight loads per lane come in groups of 8");
     __shared__ __attribute__((aligned(16))) int8_t lds[kLds];
     int8_t *xq = lds;
     uint32_t *bits = reinterpret_cast<uint32_t *>(lds + kOffBits);
@@ -187,6 +188,11 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
                 xv[u][t] = __builtin_bit_cast(uint4, load_w16(rX, ok ? 16 * (t * (K / 8) + c) : kOutOfRange));
             }
         }
+        // every wave's activation loads ahead of any weight load in the
+        // memory pipeline (a barrier on issue only: no wait for data)
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (kEarly)   // (rg = blockIdx.x < NRG: the grid is at most NRG)
             wload(0, rg);
         uint32_t fl[CPT];
@@ -382,15 +388,27 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             for (int r = 0; r < 4; r++)
                 swv[r] = sW[min(nb + r, N - 1)];
         }
-        v4i acc = {0, 0, 0, 0};
+        // fragment reads 8 at a time ahead of their MFMAs, which alternate
+        // between two accumulators (the int32 sums are exact, so splitting
+        // the dependency chain changes nothing)
+        v4i acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < KB; j++) {
-            const int q = (s0 + j) * 4 + kg;
-            v4i xf = {0, 0, 0, 0};
-            if (tok < T && s0 + j < s1 && 16 * q < K)
-                xf = *reinterpret_cast<const v4i *>(xq + q * QS + 16 * tok);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbuf[set][j], xf, acc, 0, 0, 0);
+        for (int h = 0; h < KB; h += 8) {
+            v4i xf[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int q = (s0 + h + j) * 4 + kg;
+                xf[j] = v4i{0, 0, 0, 0};
+                if (tok < T && s0 + h + j < s1 && 16 * q < K)
+                    xf[j] = *reinterpret_cast<const v4i *>(xq + q * QS + 16 * tok);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbuf[set][h + j], xf[j], acc, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbuf[set][h + j + 1], xf[j + 1], acc2, 0, 0, 0);
+            }
         }
+        acc += acc2;
         // wave 0 requests the first 32 outlier columns before the barrier
         int wr0[8];
         uint32_t xr0[8];
