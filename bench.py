@@ -118,10 +118,20 @@ def cpu_baseline(X, W, w, target_s: float, variant: str, thr: float):
     run(rows)
     dt = time.perf_counter() - t0
     ops = 2.0 * rows * w.N * w.K
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(ops / dt / 1e12, 6),
         "unit": "TOPS",
         "cores": cores,
+        "cpu_model": model,
         "kind": "oracle",
         "sample": what.format(r=rows, T=w.T) + f" ({rows}x{w.K}x{w.N}); {dt:.1f} s",
     }
