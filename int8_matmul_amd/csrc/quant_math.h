@@ -31,7 +31,14 @@ __device__ __forceinline__ float h2f(uint32_t h)
 // bit-exact against IEEE division over every such pair.
 __device__ __forceinline__ float quotient(float x, float s, float r)
 {
-    const float q0 = x * r;
+    // q0 = fl32(x*r) as an fma with a zero the compiler cannot see through,
+    // so that it folds the binary16 -> fp32 conversion of x into one
+    // mixed-precision fma (v_fma_mix_f32) instead of a convert and a
+    // multiply.  The +0 addend can only turn a -0 product into +0, i.e.
+    // only for x = 0, whose code is 0 either way.
+    float zero;
+    asm("v_mov_b32 %0, 0" : "=v"(zero));
+    const float q0 = fmaf(x, r, zero);
     const float e = fmaf(-q0, s, x);
     return fmaf(e, r, q0);
 }

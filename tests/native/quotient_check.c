@@ -5,7 +5,9 @@
  * a is the absmax (an fp16 magnitude) of the vector x belongs to, so
  * |x| <= a.  The kernels replace the per-element IEEE division by
  *     r  = fl32(1 / s)                 (once per vector, IEEE division)
- *     q0 = fl32(x * r)
+ *     q0 = fl32(x * r)                 (on the GPU fma(x, r, +0): the same
+ *                                       value for every x != 0, and x = 0
+ *                                       gives code 0 either way)
  *     e  = fma(-q0, s, x)              (exact residual)
  *     q1 = fma(e, r, q0)
  * This program checks q1 == fl32(x / s) bit for bit for every positive
