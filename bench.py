@@ -63,17 +63,33 @@ def parse():
     return ap.parse_args()
 
 
+# The headers every kernel source includes: a change in them changes the
+# kernels as much as one in the source itself.
+KERNEL_HEADERS = ["int8_matmul_amd/csrc/quant_math.h", "int8_matmul_amd/csrc/li8_internal.h"]
+
+
+def sources_sha256(paths) -> str:
+    """SHA-256 over the named files, in order (paths relative to the root)."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(hashlib.sha256(fh.read()).digest())
+    return h.hexdigest()
+
+
 def kernel_traffic(kind: str, path_src: str):
     """HBM bytes per launch of the dominant kernel from the committed
     counter summary profiles/<kind>_hbm_traffic.json, if it was taken on the
-    current kernel source; else None."""
+    current kernel source and headers; else None."""
     f = os.path.join(ROOT, "profiles", f"{kind}_hbm_traffic.json")
     if not os.path.exists(f):
         return None
     with open(f) as fh:
         rec = json.load(fh)
-    sha = hashlib.sha256(open(path_src, "rb").read()).hexdigest()
-    if rec.get("source_sha256", rec.get("gemm_source_sha256")) != sha:
+    files = rec.get("sources")
+    if not files or rec.get("sources_sha256") != sources_sha256(files):
+        return None
+    if os.path.relpath(path_src, ROOT) not in files:
         return None
     return rec.get("bytes_per_launch")
 
