@@ -296,9 +296,10 @@ li8_status smoothquant_linear(const void *X, const float *s_inv, const int8_t *W
  *                from nO on are unspecified.
  *   Xq           [T,K] int8: token codes (0 in outlier columns).
  *   sX           [T] fp32: token scales.
- *   X_out        [T,K] fp16: X_out[t,i] = X[t, outlier_idx[i]] for i < nO;
- *                columns nO .. round_up(nO,16)-1 are zero; the rest is
- *                unspecified.
+ *   X_out        T*K fp16 elements: the gathered outlier values in chunks
+ *                of 16 columns, X[t, outlier_idx[i]] at element
+ *                ((i / 16) * T + t) * 16 + i % 16 for i < nO; ranks nO ..
+ *                round_up(nO,16)-1 are zero; the rest is unspecified.
  */
 li8_status llm_int8_export_stages(const void *workspace, size_t workspace_bytes,
                                   int64_t T, int64_t K, int64_t N,

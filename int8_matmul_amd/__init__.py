@@ -496,7 +496,8 @@ def export_stages(workspace: torch.Tensor, T: int, K: int, N: int) -> dict:
         outlier_idx=torch.empty(max(K, 1), dtype=torch.int32, device=dev),
         Xq=torch.empty((T, K), dtype=torch.int8, device=dev),
         sX=torch.empty(max(T, 1), dtype=torch.float32, device=dev),
-        X_out=torch.empty((T, K), dtype=torch.float16, device=dev),
+        # gathered outlier values in 16-column chunks (see llm_int8.h)
+        X_out=torch.empty(max(T * K, 1), dtype=torch.float16, device=dev),
     )
     _check("llm_int8_export_stages",
            L.llm_int8_export_stages(_ptr(workspace), workspace.numel(), T, K, N,

@@ -362,7 +362,12 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
                 wr[e] = W16[(int64_t)wrow * K + col[e]];
             else
                 wr[e] = Wq[(int64_t)wrow * K + col[e]];
-            xr[e] = FUSED ? X[trow + col[e]] : XO_g[trow + ((i0 + e < nO) ? i0 + e : 0)];
+            if constexpr (FUSED) {
+                xr[e] = X[trow + col[e]];
+            } else {   // 16-column chunks: rank i of token t at ((i / 16) * T + t) * 16 + i % 16
+                const int i = (i0 + e < nO) ? i0 + e : 0;
+                xr[e] = XO_g[((int64_t)(i >> 4) * T + min(tok, T - 1)) * 16 + (i & 15)];
+            }
         }
     };
     auto fragments = [&](int i0, const int (&wr)[8], const uint32_t (&xr)[8], v8h &a, v8h &b) {

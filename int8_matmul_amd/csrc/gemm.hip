@@ -313,15 +313,15 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                  [&](int c) { return (int)(4u * (unsigned)(n0 + c)); });
         if (nO > 0) {   // then K >= 16: chunk 0 lies inside every row
             prefetch(rXO, PF_XO, B16{}, 2 * BM, [&](int c) {
-                return (int)((unsigned)min(m0 + (c >> 1), T - 1) * (unsigned)K * 2u + 16u * (c & 1));
+                return (int)((unsigned)min(m0 + (c >> 1), T - 1) * 32u + 16u * (c & 1));
             });
             if constexpr (F16W)
                 prefetch(rWO, PF_WO, B16{}, 2 * BN, [&](int c) {
-                    return (int)((unsigned)min(n0 + (c >> 1), N - 1) * (unsigned)K * 2u + 16u * (c & 1));
+                    return (int)((unsigned)min(n0 + (c >> 1), N - 1) * 32u + 16u * (c & 1));
                 });
             else
                 prefetch(rWO, PF_WO, B16{}, BN,
-                         [&](int c) { return (int)((unsigned)min(n0 + c, N - 1) * (unsigned)K); });
+                         [&](int c) { return (int)((unsigned)min(n0 + c, N - 1) * 16u); });
         }
     }
     if (nk > 0) {
@@ -372,27 +372,29 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     int voX[FM], voW[FN];
 #pragma unroll
     for (int a = 0; a < FM; a++)
-        voX[a] = (int)((unsigned)min(tok0 + 32 * a, T - 1) * (unsigned)K * 2u + khalf * 16u);
+        voX[a] = (int)((unsigned)min(tok0 + 32 * a, T - 1) * 32u + khalf * 16u);
 #pragma unroll
     for (int b = 0; b < FN; b++)
-        voW[b] = (int)((unsigned)min(n0 + wn * FN * 32 + 32 * b + (lane & 31), N - 1) * (unsigned)K *
-                           WOE + khalf * 8 * WOE);
+        voW[b] = (int)((unsigned)min(n0 + wn * FN * 32 + 32 * b + (lane & 31), N - 1) * 16u * WOE +
+                       khalf * 8 * WOE);
+    // chunk c of the outlier operands starts at c * cXO bytes of XO and c * cWO of WO
+    const unsigned cXO = 32u * (unsigned)T, cWO = 16u * WOE * (unsigned)N;
     v8h ox[2][FM];
     v2u ow[2][FN];     // int8 codes
     v8h ow16[2][FN];   // fp16 weight (the fp16-weight variant)
     auto oload = [&](int set, int c) {
 #pragma unroll
         for (int a = 0; a < FM; a++)
-            ox[set][a] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rXO, voX[a], c * 32, 0));
+            ox[set][a] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rXO, voX[a], (int)(cXO * (unsigned)c), 0));
         if constexpr (F16W) {
 #pragma unroll
             for (int b = 0; b < FN; b++)
                 ow16[set][b] =
-                    __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rWO, voW[b], c * 32, 0));
+                    __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rWO, voW[b], (int)(cWO * (unsigned)c), 0));
         } else {
 #pragma unroll
             for (int b = 0; b < FN; b++)
-                ow[set][b] = __builtin_amdgcn_raw_buffer_load_b64(rWO, voW[b], c * 16, 0);
+                ow[set][b] = __builtin_amdgcn_raw_buffer_load_b64(rWO, voW[b], (int)(cWO * (unsigned)c), 0);
         }
     };
     // chunk 0 from the prefetch

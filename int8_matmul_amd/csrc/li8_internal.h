@@ -29,12 +29,13 @@ constexpr int kDecodeMaxBlocks = 256;   // one workgroup per CU
 //   idx  : int32[K]            outlier columns, ascending
 //   sX   : fp32[T]             token scales
 //   Xq   : int8[T,K]           token codes, 0 in outlier columns
-//   XO   : fp16[T,K]           X[t, idx[i]] at column i < nO, zero pad to a
-//                              multiple of 16; row stride K
-//   WO   : int8[N,K]           Wq[n, idx[i]] at column i < nO, zero pad to a
-//                              multiple of 16; row stride K.  In the fp16-weight
-//                              variant the same region holds fp16[N,K] with
-//                              W[n, idx[i]] (hence 2*N*K bytes)
+//   XO   : fp16, T*K elements  the gathered outlier values in 16-column
+//                              chunks: X[t, idx[i]] at ((i/16)*T + t)*16 + i%16
+//                              for i < nO, zero to the next multiple of 16
+//                              (a chunk of a row block is contiguous)
+//   WO   : int8, N*K elements  likewise Wq[n, idx[i]] at ((i/16)*N + n)*16 +
+//                              i%16.  In the fp16-weight variant the same
+//                              region holds fp16 W[n, idx[i]] (2*N*K bytes)
 struct WsLayout {
     size_t bits, meta, idx, sX, Xq, XO, WO, total;
 };
@@ -60,7 +61,7 @@ inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
 //   hdr  : int32[64]  hdr[0] = 1 when it holds a set, [1] its nO,
 //                     [2] hits, [3] misses (calls that gathered)
 //   bits : uint32[ceil(K/32)]  the cached outlier bit set
-//   WO   : int8[N,K]  Wq[n, idx[i]] at column i < nO, zero pad to 16
+//   WO   : int8, N*K elements, the workspace WO layout (16-column chunks)
 struct CacheLayout {
     size_t hdr, bits, WO, total;
 };

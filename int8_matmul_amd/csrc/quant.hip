@@ -316,7 +316,9 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
             if (tid == 0)
                 sX[t] = sc;
             uint2 *q = reinterpret_cast<uint2 *>(Xq + t * K);
-            uint16_t *xo = XO + t * K;
+            // outlier values in 16-column chunks: rank i of row t at
+            // ((i / 16) * T + t) * 16 + i % 16
+            auto xo = [&](int i) -> uint16_t & { return XO[((int64_t)(i >> 4) * T + t) * 16 + (i & 15)]; };
             auto emit = [&](int c, uint4 x) {
                 const uint32_t wbits = bits[c >> 2];
                 const uint32_t skip = (wbits >> (8 * (c & 3))) & 0xffu;
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
 #pragma unroll
                     for (int e = 0; e < 8; e++)
                         if ((skip >> e) & 1u)
-                            xo[i++] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                            xo(i++) = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
                 }
             };
 #pragma unroll
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
             for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads)
                 emit(c, xr[c]);
             if (tid < nO16 - nO)
-                xo[nO + tid] = 0;
+                xo(nO + tid) = 0;
         }
         return;
     }
@@ -419,18 +421,19 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
                 hw[4 * q + 2] = v.z;
                 hw[4 * q + 3] = v.w;
             }
-            uint16_t *dst = WO16 + (int64_t)n * K;
+            // (16-column chunks: rank i of row n at ((i / 16) * N + n) * 16 + i % 16)
             int i = pre[w];
             while (b) {
                 const int j = __ffs(b) - 1;
-                dst[i++] = (uint16_t)((hw[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                WO16[((int64_t)(i >> 4) * N + n) * 16 + (i & 15)] = (uint16_t)((hw[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                i++;
                 b &= b - 1u;
             }
         }
         for (int p = tid; p < (n1 - n0) * 16; p += kThreads) {
             const int n = n0 + p / 16, e = p % 16;
             if (nO + e < nO16)
-                WO16[(int64_t)n * K + nO + e] = 0;
+                WO16[((int64_t)((nO + e) >> 4) * N + n) * 16 + ((nO + e) & 15)] = 0;
         }
         return;
     }
@@ -444,18 +447,19 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
         if (32 * w + 16 < K)
             hi = *reinterpret_cast<const uint4 *>(src + 16);
         const uint32_t by[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        int8_t *dst = WO + (int64_t)n * K;
+        // (16-column chunks: rank i of row n at ((i / 16) * N + n) * 16 + i % 16)
         int i = pre[w];
         while (b) {
             const int j = __ffs(b) - 1;
-            dst[i++] = (int8_t)((by[j >> 2] >> (8 * (j & 3))) & 0xffu);
+            WO[((int64_t)(i >> 4) * N + n) * 16 + (i & 15)] = (int8_t)((by[j >> 2] >> (8 * (j & 3))) & 0xffu);
+            i++;
             b &= b - 1u;
         }
     }
     for (int p = tid; p < (n1 - n0) * 16; p += kThreads) {
         const int n = n0 + p / 16, e = p % 16;
         if (nO + e < nO16)
-            WO[(int64_t)n * K + nO + e] = 0;
+            WO[((int64_t)((nO + e) >> 4) * N + n) * 16 + ((nO + e) & 15)] = 0;
     }
 }
 

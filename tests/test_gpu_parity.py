@@ -71,6 +71,16 @@ def gpu_run(X, W, thr):
     return r
 
 
+def chunks_to_rows(flat, T, nO):
+    """[T, round_up(nO, 16)] from the 16-column chunk layout of the gathered
+    outlier values: rank i of row t at ((i // 16) * T + t) * 16 + i % 16."""
+    n16 = (nO + 15) // 16 * 16
+    out = np.zeros((T, n16), dtype=flat.dtype)
+    for c in range(n16 // 16):
+        out[:, 16 * c:16 * c + 16] = flat[c * T * 16:(c + 1) * T * 16].reshape(T, 16)
+    return out
+
+
 def check_full(X, W, thr, label):
     say(f"case {label}: T={X.shape[0]} K={X.shape[1]} N={W.shape[0]} thr={thr}")
     T, K = X.shape
@@ -85,9 +95,9 @@ def check_full(X, W, thr, label):
     assert np.array_equal(g["outlier_idx"][:nO], o["idx"]), "outlier index list"
     assert np.array_equal(g["Xq"], o["Xq"]), "token codes"
     assert np.array_equal(g["sX"][:T], o["sX"]), "token scales"
-    assert np.array_equal(g["X_out"][:, :nO], X[:, o["idx"]]), "gathered outlier columns"
-    nO16 = (nO + 15) // 16 * 16
-    assert np.all(g["X_out"][:, nO:nO16].view(np.uint16) == 0), "zero pad of the gather"
+    XO = chunks_to_rows(g["X_out"], T, nO)
+    assert np.array_equal(XO[:, :nO], X[:, o["idx"]]), "gathered outlier columns"
+    assert np.all(XO[:, nO:].view(np.uint16) == 0), "zero pad of the gather"
     assert np.array_equal(g["acc"], o["acc"]), "int32 accumulators"
     assert np.array_equal(g["Y"].view(np.uint16), g["Y_fused"].view(np.uint16)), \
         "prepare+gemm and the fused call differ"
