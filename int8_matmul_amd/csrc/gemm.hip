@@ -285,11 +285,9 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     using WS = std::integral_constant<int, (LA + LB) * (NS - 2)>;
 
     const int nk = (K + BKS - 1) / BKS;
-#pragma unroll
-    for (int s = 0; s < NS; s++)
-        if (s < nk)
-            issue(s);
-    // epilogue prefetch (after the first stages, so that they land first);
+    // epilogue prefetch, issued ahead of the first stages: loads complete in
+    // order, so once all but the last LA+LB loads of a lane are done, stage
+    // 0 and the prefetch have landed while stage 1 may still be in flight;
     // rows past T or N read zeros or clamp, and are never stored
     const __amdgpu_buffer_rsrc_t rXO = make_rsrc(XO, (int)(2u * (unsigned)T * (unsigned)K));
     const __amdgpu_buffer_rsrc_t rWO = make_rsrc(WO, (int)((unsigned)WOE * (unsigned)N * (unsigned)K));
@@ -324,7 +322,14 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                          [&](int c) { return (int)((unsigned)min(n0 + c, N - 1) * 16u); });
         }
     }
-    if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+        if (s < nk)
+            issue(s);
+    if (nk >= NS) {
+        wait_loads_barrier<(NS - 1) * (LA + LB)>();   // stage 0 landed
+        lread(0, 0, 0);
+    } else if (nk > 0) {
         wait_loads_barrier<0>();
         lread(0, 0, 0);
     }
