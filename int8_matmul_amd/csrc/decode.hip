@@ -62,7 +62,9 @@ constexpr int kOffRx = kOffSx + 4 * kDMaxT;               // float[16] their rec
 constexpr int kOffRed = kOffRx + 4 * kDMaxT;              // v4i[2][8][64]
 constexpr int kIdxCap = 1024;                             // outlier columns listed in LDS
 constexpr int kOffIdx = kOffRed + 2 * kDWaves * 64 * 16;  // int32[kIdxCap]
-constexpr int kLds = kOffIdx + 4 * kIdxCap;
+constexpr int kMaxCpt = kDMaxK / (8 * kDThreads);         // 8-column chunks per thread
+constexpr int kOffOcnt = kOffIdx + 4 * kIdxCap;           // int32[kMaxCpt][8] outlier columns per wave
+constexpr int kLds = kOffOcnt + 4 * kMaxCpt * kDWaves;
 static_assert(kLds <= 160 * 1024, "LDS of one workgroup");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes)
@@ -130,6 +132,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     float *sxl = reinterpret_cast<float *>(lds + kOffSx);
     float *rxl = reinterpret_cast<float *>(lds + kOffRx);
     int32_t *idxl = reinterpret_cast<int32_t *>(lds + kOffIdx);
+    int32_t *ocnt = reinterpret_cast<int32_t *>(lds + kOffOcnt);
     v4i *red = reinterpret_cast<v4i *>(lds + kOffRed);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -175,8 +178,8 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     int nO;
     if constexpr (FUSED) {
         constexpr int CPT = KB / 8;   // 8-column chunks per thread: K <= 4096*CPT
+        static_assert(CPT <= kMaxCpt, "chunks per thread");
         const int nchunk = K / 8;
-        const int nw = (K + 31) / 32;
         const __amdgpu_buffer_rsrc_t rX = make_rsrc(X, 2 * T * K);
         uint4 xv[CPT][TB];
 #pragma unroll
@@ -196,6 +199,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         if constexpr (kEarly)   // (rg = blockIdx.x < NRG: the grid is at most NRG)
             wload(0, rg);
         uint32_t fl[CPT];
+        int orank[CPT];   // outlier columns before this chunk's, within this wave and pass u
         uint32_t rm[TB];
 #pragma unroll
         for (int t = 0; t < TB; t++)
@@ -214,6 +218,23 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             word |= (uint32_t)__shfl_xor((int)word, 2, 64);
             if ((c & 3) == 0 && c < nchunk)
                 bits[c >> 2] = word;
+            // ranks of the outlier columns: chunks are ordered by (u, tid),
+            // so an exclusive prefix of the per-chunk counts (0..8) over the
+            // lanes, bit by bit with ballots, and per-wave totals in LDS
+            {
+                const int cnt = __popc(fl[u]);
+                const uint64_t below = (1ull << lane) - 1ull;
+                int p = 0, tot = 0;
+#pragma unroll
+                for (int bit = 0; bit < 4; bit++) {
+                    const uint64_t m = __ballot((cnt >> bit) & 1);
+                    p += __popcll(m & below) << bit;
+                    tot += __popcll(m) << bit;
+                }
+                orank[u] = p;
+                if (lane == 0)
+                    ocnt[u * kDWaves + wid] = tot;
+            }
 #pragma unroll
             for (int t = 0; t < TB; t++)
                 rm[t] = max(rm[t], chunk_max(xv[u][t], fl[u]));
@@ -249,52 +270,52 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             sx[t] = sxl[t];
             rx[t] = rxl[t];
         }
+        // nO and the rank of this thread's first outlier column in each pass
+        nO = 0;
+#pragma unroll
+        for (int u = 0; u < CPT; u++) {
+            int before = 0, pass = 0;   // this pass: waves before this one, all waves
+#pragma unroll
+            for (int w = 0; w < kDWaves; w++) {
+                const int v = ocnt[u * kDWaves + w];
+                before += (w < wid) ? v : 0;
+                pass += v;
+            }
+            orank[u] += nO + before;
+            nO += pass;
+        }
 #pragma unroll
         for (int u = 0; u < CPT; u++) {
             const int c = tid + u * kDThreads;
+            const uint2 keep = keep_bytes8(fl[u]);   // the chunk's columns are the same for every token
             if (c < nchunk) {
 #pragma unroll
                 for (int t = 0; t < TB; t++)
                     if (t < T) {
                         const uint2 q = (sx[t] == 0.0f) ? make_uint2(0u, 0u)
-                                                        : token_codes8(xv[u][t], fl[u], sx[t], rx[t]);
+                                                        : token_codes8_keep(xv[u][t], keep, sx[t], rx[t]);
                         *reinterpret_cast<uint2 *>(xq + (c >> 1) * QS + 16 * t + 8 * (c & 1)) = q;
                     }
             }
         }
-        lds_barrier();
-        // exclusive prefix counts of the bit-set words, for the outlier
-        // column ranks (only wave 0 uses them)
-        nO = 0;
-        if (wid == 0) {
-            const int per = (nw + 63) / 64;
-            const int w0 = min(nw, lane * per), w1 = min(nw, w0 + per);
-            int cnt = 0;
-            for (int w = w0; w < w1; w++)
-                cnt += __popc(bits[w]);
-            // exclusive prefix of cnt (< 256) over the lanes, bit by bit
-            // with ballots: no LDS round trips
-            const uint64_t below = (1ull << lane) - 1ull;
-            int p = 0;
-            nO = 0;
+        // the ascending list of outlier columns (while it fits in LDS), and
+        // the rank of each bit-set word's first column for the rank search
+        // past that; each thread writes its own chunks' entries
 #pragma unroll
-            for (int bit = 0; bit < 8; bit++) {
-                const uint64_t m = __ballot((cnt >> bit) & 1);
-                p += __popcll(m & below) << bit;
-                nO += __popcll(m) << bit;
-            }
-            for (int w = w0; w < w1; w++) {
-                pre[w] = p;
-                uint32_t b = bits[w];
-                if (nO <= kIdxCap)   // the ascending list of outlier columns
-                    while (b) {
-                        idxl[p++] = 32 * w + __ffs(b) - 1;
-                        b &= b - 1u;
-                    }
-                else
-                    p += __popc(b);
+        for (int u = 0; u < CPT; u++) {
+            const int c = tid + u * kDThreads;
+            if ((c & 3) == 0 && c < nchunk)
+                pre[c >> 2] = orank[u];
+            if (nO <= kIdxCap) {
+                uint32_t b = fl[u];
+                int p = orank[u];
+                while (b) {
+                    idxl[p++] = 8 * c + __ffs(b) - 1;
+                    b &= b - 1u;
+                }
             }
         }
+        lds_barrier();
     } else {
         // token codes of the prepared workspace into the LDS layout: up to
         // 16 chunks of 16 bytes per thread (T*K/16 <= 16*512)

@@ -86,6 +86,31 @@ __device__ __forceinline__ uint2 token_codes8(uint4 v, uint32_t skip, float s, f
     return make_uint2(pack_low_bytes(c[0], c[1], c[2], c[3]), pack_low_bytes(c[4], c[5], c[6], c[7]));
 }
 
+// Byte masks for the 8 codes of a chunk: byte e of the result (x: bytes
+// 0-3, y: bytes 4-7) is 0xff when bit e of `skip` is clear and 0 when it is
+// set.  (Multiplying a 4-bit value by 0x00204081 places its bit b at bit
+// 8b with no carries; the mask keeps those bits and *0xff widens them.)
+__device__ __forceinline__ uint2 keep_bytes8(uint32_t skip)
+{
+    const uint32_t lo = ((skip & 0xfu) * 0x00204081u) & 0x01010101u;
+    const uint32_t hi = (((skip >> 4) & 0xfu) * 0x00204081u) & 0x01010101u;
+    return make_uint2(~(lo * 0xffu), ~(hi * 0xffu));
+}
+
+// Codes of a chunk as token_codes8, with the outlier positions cleared by
+// byte masks from keep_bytes8 (for a caller that quantizes several tokens
+// over the same columns and builds the masks once).
+__device__ __forceinline__ uint2 token_codes8_keep(uint4 v, uint2 keep, float s, float r)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        c[e] = code_bits((w[e >> 1] >> (16 * (e & 1))) & 0xffffu, s, r);
+    return make_uint2(pack_low_bytes(c[0], c[1], c[2], c[3]) & keep.x,
+                      pack_low_bytes(c[4], c[5], c[6], c[7]) & keep.y);
+}
+
 // Max magnitude of the 8 binary16 values in v whose bit in `skip` is clear.
 __device__ __forceinline__ uint32_t masked_max8(uint4 v, uint32_t skip)
 {
