@@ -134,6 +134,22 @@ def cpu_baseline(X, W, w, target_s: float, variant: str, thr: float):
     run(rows)
     dt = time.perf_counter() - t0
     ops = 2.0 * rows * w.N * w.K
+    # the oracle's quantize stage on the whole of X, timed on its own:
+    # detection and token quantization (sq: the smoothed token quantization),
+    # against the same algorithmic bytes as the GPU's stage minus the
+    # outlier gathers
+    T, K = X.shape
+    t0 = time.perf_counter()
+    if variant == "sq":
+        oracle.sq_quantize_rows(X, s)
+        qbytes = 2 * T * K + 4 * K + T * K + 4 * T
+        qwhat = "smoothed token quantization of all of X"
+    else:
+        flags, _ = oracle.detect_outliers(X, thr)
+        oracle.quantize_rows(X, flags)
+        qbytes = 2 * T * K + 2 * T * K + T * K + 4 * T
+        qwhat = "detection and token quantization of all of X (no outlier gathers)"
+    qdt = time.perf_counter() - t0
     model = None
     try:
         with open("/proc/cpuinfo") as fh:
@@ -150,6 +166,8 @@ def cpu_baseline(X, W, w, target_s: float, variant: str, thr: float):
         "cpu_model": model,
         "kind": "oracle",
         "sample": what.format(r=rows, T=w.T) + f" ({rows}x{w.K}x{w.N}); {dt:.1f} s",
+        "quant_gbps": round(qbytes / qdt / 1e9, 3),
+        "quant_sample": f"{qwhat} ({T}x{K}); {qdt * 1e3:.1f} ms",
     }
 
 
