@@ -77,11 +77,11 @@ def sources_sha256(paths) -> str:
     return h.hexdigest()
 
 
-def kernel_traffic(kind: str, path_src: str):
-    """HBM bytes per launch of the dominant kernel from the committed
-    counter summary profiles/<kind>_hbm_traffic.json, if it was taken on the
-    current kernel source and headers; else None."""
-    f = os.path.join(ROOT, "profiles", f"{kind}_hbm_traffic.json")
+def profile_record(name: str, path_src: str, workload: str):
+    """The committed counter summary profiles/<name>.json, if it was taken
+    on the current kernel source and headers and on this workload; else
+    None."""
+    f = os.path.join(ROOT, "profiles", f"{name}.json")
     if not os.path.exists(f):
         return None
     with open(f) as fh:
@@ -89,9 +89,30 @@ def kernel_traffic(kind: str, path_src: str):
     files = rec.get("sources")
     if not files or rec.get("sources_sha256") != sources_sha256(files):
         return None
-    if os.path.relpath(path_src, ROOT) not in files:
+    if os.path.relpath(path_src, ROOT) not in files or rec.get("workload_name") != workload:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def kernel_traffic(kind: str, path_src: str, workload: str):
+    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE
+    scaled by a copy of known size) from profiles/<kind>_hbm_traffic.json."""
+    rec = profile_record(f"{kind}_hbm_traffic", path_src, workload)
+    return rec.get("bytes_per_launch") if rec else None
+
+
+def clock_adjusted(path_src: str, workload: str, achieved: float):
+    """The int8 peak at the shader clock the GEMM ran at in the committed
+    counter run (SQ_BUSY_CYCLES per shader engine over the launch time,
+    profiles/gemm_sclk.json), and the fraction of it achieved here."""
+    rec = profile_record("gemm_sclk", path_src, workload)
+    if not rec:
+        return None
+    ghz = float(rec["sclk_ghz"])
+    peak = PEAK_INT8_TOPS * ghz / 2.4
+    return {"sclk_ghz": ghz, "peak": round(peak, 1), "frac": round(achieved / peak, 4),
+            "sclk_from": "profiles/gemm_sclk.json: SQ_BUSY_CYCLES per shader engine over the "
+                         "profiled k_gemm launches (the 5.0 POP/s peak assumes 2.4 GHz)"}
 
 
 def cpu_baseline(X, W, w, target_s: float, variant: str, thr: float):
@@ -423,7 +444,7 @@ def main():
                               "int8 MFMA, outlier MFMA, epilogue)",
                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                    "traffic": kernel_traffic("decode", src) if args.variant == "int8w" else None}
+                    "traffic": kernel_traffic("decode", src, args.workload) if args.variant == "int8w" else None}
     else:
         src = os.path.join(ROOT, "int8_matmul_amd", "csrc", "gemm.hip")
         roofline = {"bound": "mfma",
@@ -431,7 +452,9 @@ def main():
                     "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                     # counters taken on the LLM.int8() call only
-                    "traffic": kernel_traffic("gemm", src) if args.variant == "int8w" else None}
+                    "traffic": kernel_traffic("gemm", src, args.workload) if args.variant == "int8w" else None,
+                    "clock_adjusted": (clock_adjusted(src, args.workload, gemm_tops)
+                                       if args.variant == "int8w" else None)}
 
     entry = {"sq": "smoothquant_linear", "cached": "llm_int8_linear_cached",
              "fp16w": "llm_int8_linear_fp16w"}.get(args.variant, "llm_int8_linear")
