@@ -483,25 +483,26 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         }
         if (tok >= T)
             return;
-        uint32_t h[4];
+        float p[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             // fl32(D * sW) first, then one rounding to fp16 (the empty asm
             // keeps the product and the conversion from being fused)
-            float p = d[r];
+            p[r] = d[r];
             if constexpr (!F16W)
-                p *= swv[r];
-            asm("" : "+v"(p));
-            h[r] = __builtin_bit_cast(uint16_t, (_Float16)p);
+                p[r] *= swv[r];
+            asm("" : "+v"(p[r]));
         }
+        const uint32_t h01 = pack_f16x2(p[0], p[1]), h23 = pack_f16x2(p[2], p[3]);
         uint16_t *y = Y + (int64_t)tok * N + nb;
         if ((N & 3) == 0 && nb + 3 < N) {
-            *reinterpret_cast<uint2 *>(y) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            *reinterpret_cast<uint2 *>(y) = make_uint2(h01, h23);
         } else {
+            const uint32_t hw[2] = {h01, h23};
 #pragma unroll
             for (int r = 0; r < 4; r++)
                 if (nb + r < N)
-                    y[r] = (uint16_t)h[r];
+                    y[r] = (uint16_t)(hw[r >> 1] >> (16 * (r & 1)));
         }
     };
 

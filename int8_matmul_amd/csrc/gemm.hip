@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "li8_internal.h"
+#include "quant_math.h"
 
 namespace li8 {
 namespace {
@@ -506,21 +507,20 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const float s4[4] = {sw[b][g].x, sw[b][g].y, sw[b][g].z, sw[b][g].w};
-                uint32_t h[4];
+                float p[4];
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     // fl32(D * sW) first, then one rounding to fp16: the
                     // empty asm keeps the compiler from fusing the product
                     // and the conversion into a single-rounding
                     // v_fma_mixlo_f16
-                    float p = d[a][b][4 * g + j];
+                    p[j] = d[a][b][4 * g + j];
                     if constexpr (!F16W)
-                        p *= s4[j];
-                    asm("" : "+v"(p));
-                    h[j] = __builtin_bit_cast(uint16_t, (_Float16)p);
+                        p[j] *= s4[j];
+                    asm("" : "+v"(p[j]));
                 }
                 *reinterpret_cast<uint2 *>(stg + (a * 32 + (lane & 31)) * RS + b * 32 + 8 * g +
-                                           4 * khalf) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                                           4 * khalf) = make_uint2(pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]));
             }
     // each wave stores its own sub-tile (only its own LDS rows: no barrier)
     constexpr int CPRW = FN * 32 / 8;   // 16-byte chunks per sub-tile row

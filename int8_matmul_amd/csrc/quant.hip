@@ -534,9 +534,14 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
     const int nchunk = (int)(K / 8);
     if (nchunk > 0) {
         const int gx = (nchunk + kThreads - 1) / kThreads;
-        // rows per block: a multiple of the load batch, about 256
-        // workgroups in all (measured fastest), grid.y <= 65535
-        int gy = (int)std::min<int64_t>((T + kDetectRows - 1) / kDetectRows, std::max(1, 256 / gx));
+        // rows per block: a multiple of the load batch.  Two batches per
+        // block when that still gives at least 256 workgroups (measured
+        // fastest at 4096 x 4096 and 4096 x 8192), else about 256
+        // workgroups of one batch; grid.y <= 65535
+        const int64_t gy2 = (T + 2 * kDetectRows - 1) / (2 * kDetectRows);
+        int gy = gx * gy2 >= 256
+                     ? (int)std::min<int64_t>(gy2, 65535)
+                     : (int)std::min<int64_t>((T + kDetectRows - 1) / kDetectRows, std::max(1, 256 / gx));
         int R = (int)((T + gy - 1) / gy);
         R = (R + kDetectRows - 1) / kDetectRows * kDetectRows;
         while ((T + R - 1) / R > 65535)

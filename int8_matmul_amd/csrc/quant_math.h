@@ -62,6 +62,16 @@ __device__ __forceinline__ uint32_t code_bits(uint32_t h, float s, float r)
     return __builtin_bit_cast(uint32_t, quotient(h2f(h), s, r) + 12582912.0f);
 }
 
+// Two fp32 values rounded to binary16 (nearest even) and packed, a in the
+// low half: one v_cvt_pk_f16_f32, which rounds as the scalar conversion
+// does (checked over every fp32 bit pattern apart from NaN payloads).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
+{
+    typedef float li8_f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 li8_h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((li8_f2){a, b}, li8_h2));
+}
+
 // Low bytes of four words packed into one (v_perm_b32 byte selects).
 __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
