@@ -358,7 +358,11 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     // values (weight code of row wrow, binary16 of token tok; clamped,
     // always valid addresses), then the MFMA fragments with the ranks past
     // nO (and padding tokens) zeroed.
-    auto gather_raw = [&](int wrow, int i0, int (&wr)[8], uint32_t (&xr)[8]) {
+    // Only wave 0 uses them (`active`); the loads are buffer loads issued by
+    // every wave, with an out-of-range offset (zeros, nothing fetched)
+    // where inactive: in a branch, the compiler would wait for them at the
+    // join instead of at their use after the reduction barrier.
+    auto gather_raw = [&](int rgc, int i0, bool active, int (&wr)[8], uint32_t (&xr)[8]) {
         int col[8];
         if constexpr (FUSED) {
             if (nO <= kIdxCap) {
@@ -372,23 +376,48 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
                     col[e] = max(col[e], 0);
             }
         } else {
+            const __amdgpu_buffer_rsrc_t rI = make_rsrc(idx_g, 4 * K);
+            uint32_t ioff_hi = active ? 0u : 0x80000000u;   // (as for the data loads below)
+            asm volatile("" : "+v"(ioff_hi));
 #pragma unroll
             for (int e = 0; e < 8; e++)
-                col[e] = (i0 + e < nO) ? min(max(idx_g[i0 + e], 0), K - 1) : 0;
+                col[e] = min(max((int)__builtin_amdgcn_raw_buffer_load_b32(
+                                     rI, (int)((uint32_t)(i0 + e < nO ? 4 * (i0 + e) : kOutOfRange) | ioff_hi),
+                                     0, 0),
+                                 0),
+                             K - 1);
         }
-        const int64_t trow = (int64_t)min(tok, T - 1) * K;
+        // weight rows of this row group (at most 16 rows of K elements from
+        // its first row, so the offsets stay small), token rows of X / XO
+        const int rows = min(kDRows, N - rgc * kDRows);
+        const int wl = min(rgc * kDRows + (lane & 15), N - 1) - rgc * kDRows;   // local weight row
+        const __amdgpu_buffer_rsrc_t rWg =
+            F16W ? make_rsrc(W16 + (int64_t)rgc * kDRows * K, 2 * rows * K)
+                 : make_rsrc(Wq + (int64_t)rgc * kDRows * K, rows * K);
+        const int ttok = min(tok, T - 1);
+        const __amdgpu_buffer_rsrc_t rXg = FUSED ? make_rsrc(X, 2 * T * K) : make_rsrc(XO_g, 2 * T * K);
+        // bit 31 set in every offset of an inactive wave (past any buffer);
+        // opaque to the compiler, which would otherwise branch on `active`
+        uint32_t off_hi = active ? 0u : 0x80000000u;
+        asm volatile("" : "+v"(off_hi));
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            if constexpr (F16W)
-                wr[e] = W16[(int64_t)wrow * K + col[e]];
-            else
-                wr[e] = Wq[(int64_t)wrow * K + col[e]];
+            const bool ok = i0 + e < nO;
+            const int wo = wl * K + col[e];
+            int xo;
             if constexpr (FUSED) {
-                xr[e] = X[trow + col[e]];
+                xo = ttok * K + col[e];
             } else {   // 16-column chunks: rank i of token t at ((i / 16) * T + t) * 16 + i % 16
-                const int i = (i0 + e < nO) ? i0 + e : 0;
-                xr[e] = XO_g[((int64_t)(i >> 4) * T + min(tok, T - 1)) * 16 + (i & 15)];
+                const int i = i0 + e;
+                xo = ((i >> 4) * T + ttok) * 16 + (i & 15);
             }
+            const int woff = (int)((uint32_t)(ok ? (F16W ? 2 * wo : wo) : kOutOfRange) | off_hi);
+            const int xoff = (int)((uint32_t)(ok ? 2 * xo : kOutOfRange) | off_hi);
+            if constexpr (F16W)
+                wr[e] = __builtin_amdgcn_raw_buffer_load_b16(rWg, woff, 0, 0);
+            else
+                wr[e] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(rWg, woff, 0, 0);
+            xr[e] = __builtin_amdgcn_raw_buffer_load_b16(rXg, xoff, 0, 0);
         }
     };
     auto fragments = [&](int i0, const int (&wr)[8], const uint32_t (&xr)[8], v8h &a, v8h &b) {
@@ -407,13 +436,23 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // wave 0 requests its feature scales first, so that they arrive
         // during the MFMAs
         const int nb = rgc * kDRows + 4 * kg;   // this lane's first feature
-        const int wrow = min(rgc * kDRows + (lane & 15), N - 1);
         float swv[4];
-        if (wid == 0) {
+        {
+            const __amdgpu_buffer_rsrc_t rS = make_rsrc(sW, 4 * N);
+            uint32_t soff_hi = wid == 0 ? 0u : 0x80000000u;   // (see gather_raw)
+            asm volatile("" : "+v"(soff_hi));
 #pragma unroll
             for (int r = 0; r < 4; r++)
-                swv[r] = sW[min(nb + r, N - 1)];
+                swv[r] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(
+                               rS, (int)((uint32_t)(4 * min(nb + r, N - 1)) | soff_hi), 0, 0));
         }
+        // wave 0 requests the first 32 outlier columns before its MFMAs
+        // (loads complete in order; the MFMAs wait only for the older
+        // weight loads)
+        int wr0[8];
+        uint32_t xr0[8];
+        gather_raw(rgc, 8 * kg, wid == 0, wr0, xr0);
         // fragment reads 8 at a time ahead of their MFMAs, which alternate
         // between two accumulators (the int32 sums are exact, so splitting
         // the dependency chain changes nothing)
@@ -435,11 +474,6 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             }
         }
         acc += acc2;
-        // wave 0 requests the first 32 outlier columns before the barrier
-        int wr0[8];
-        uint32_t xr0[8];
-        if (wid == 0 && nO > 0)
-            gather_raw(wrow, 8 * kg, wr0, xr0);
         red[(par * kDWaves + wid) * 64 + lane] = acc;
         lds_barrier();
         if (wid != 0)
@@ -476,7 +510,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             } else {
                 int wr[8];
                 uint32_t xr[8];
-                gather_raw(wrow, i0, wr, xr);
+                gather_raw(rgc, i0, true, wr, xr);
                 fragments(i0, wr, xr, a, b);
             }
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, d, 0, 0, 0);
@@ -506,9 +540,14 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         }
     };
 
-    // two row groups per iteration, so that the register set holding the
-    // next group's weights is fixed at compile time; the next group's loads
-    // are issued before this group's MFMAs
+    // One row group per workgroup (N <= 16 x grid): no next group to load.
+    if (NRG <= G) {
+        process(0, rg, 0);
+        return;
+    }
+    // Else two row groups per iteration, so that the register set holding
+    // the next group's weights is fixed at compile time; the next group's
+    // loads are issued before this group's MFMAs
     while (rg < NRG) {
         const int rg1 = rg + G;
         wload(1, rg1);   // zeros past the last group
