@@ -60,11 +60,16 @@ constexpr int kOffRmax = kOffPre + 4 * (kDMaxK / 32);     // uint32[8][16]
 constexpr int kOffSx = kOffRmax + 4 * kDWaves * kDMaxT;   // float[16] token scales
 constexpr int kOffRx = kOffSx + 4 * kDMaxT;               // float[16] their reciprocals
 constexpr int kOffRed = kOffRx + 4 * kDMaxT;              // v4i[2][8][64]
-constexpr int kIdxCap = 1024;                             // outlier columns listed in LDS
+constexpr int kIdxCap = 512;                              // outlier columns listed in LDS
 constexpr int kOffIdx = kOffRed + 2 * kDWaves * 64 * 16;  // int32[kIdxCap]
 constexpr int kMaxCpt = kDMaxK / (8 * kDThreads);         // 8-column chunks per thread
 constexpr int kOffOcnt = kOffIdx + 4 * kIdxCap;           // int32[kMaxCpt][8] outlier columns per wave
-constexpr int kLds = kOffOcnt + 4 * kMaxCpt * kDWaves;
+// the first 32 outlier columns of the row group's 16 weight rows and of the
+// 16 token slots, and the group's 16 column scales, gathered by all threads
+constexpr int kOffGw = kOffOcnt + 4 * kMaxCpt * kDWaves;  // uint16[16][32] code bytes (or fp16 weights)
+constexpr int kOffGx = kOffGw + 2 * 16 * 32;              // uint16[16][32] fp16 activations
+constexpr int kOffGs = kOffGx + 2 * 16 * 32;              // float[16]
+constexpr int kLds = kOffGs + 4 * kDRows;
 static_assert(kLds <= 160 * 1024, "LDS of one workgroup");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes)
@@ -133,6 +138,9 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     float *rxl = reinterpret_cast<float *>(lds + kOffRx);
     int32_t *idxl = reinterpret_cast<int32_t *>(lds + kOffIdx);
     int32_t *ocnt = reinterpret_cast<int32_t *>(lds + kOffOcnt);
+    uint16_t *gwl = reinterpret_cast<uint16_t *>(lds + kOffGw);
+    uint16_t *gxl = reinterpret_cast<uint16_t *>(lds + kOffGx);
+    float *gsl = reinterpret_cast<float *>(lds + kOffGs);
     v4i *red = reinterpret_cast<v4i *>(lds + kOffRed);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -176,6 +184,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     // them after it.)
     constexpr bool kEarly = !(FUSED && KB > 8 && TB > 8);
     int nO;
+    int g_idx = 0;   // workspace path: column of outlier rank tid % 32 (loaded before the weights)
     if constexpr (FUSED) {
         constexpr int CPT = KB / 8;   // 8-column chunks per thread: K <= 4096*CPT
         static_assert(CPT <= kMaxCpt, "chunks per thread");
@@ -335,6 +344,10 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // so a later load would wait for the whole weight batch
         const float sxg = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rS, tid < T ? 4 * tid : kOutOfRange, 0, 0));
+        // and the first 32 outlier columns' indices, which the epilogue
+        // gathers are addressed by
+        g_idx = (int)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(idx_g, 4 * K),
+                                                          (tid & 31) < nO ? 4 * (tid & 31) : kOutOfRange, 0, 0);
         wload(0, rg);
 #pragma unroll
         for (int j = 0; j < TB; j++) {
@@ -353,16 +366,11 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         wload(0, rg);
 
     // ---- row groups: int8 MFMAs over this wave's share of K ----
-    // Outlier operands of 8 consecutive ranks from i0 for this lane, in two
-    // steps so that the loads can be in flight across a barrier: the raw
-    // values (weight code of row wrow, binary16 of token tok; clamped,
-    // always valid addresses), then the MFMA fragments with the ranks past
-    // nO (and padding tokens) zeroed.
-    // Only wave 0 uses them (`active`); the loads are buffer loads issued by
-    // every wave, with an out-of-range offset (zeros, nothing fetched)
-    // where inactive: in a branch, the compiler would wait for them at the
-    // join instead of at their use after the reduction barrier.
-    auto gather_raw = [&](int rgc, int i0, bool active, int (&wr)[8], uint32_t (&xr)[8]) {
+    // Outlier operands of 8 consecutive ranks from i0 for this lane (wave 0,
+    // outlier chunks past the first): the raw values (weight of this lane's
+    // row, binary16 of token tok; buffer loads, zeros past the ends), then
+    // the MFMA fragments with the ranks past nO (and padding tokens) zeroed.
+    auto gather_raw = [&](int rgc, int i0, int (&wr)[8], uint32_t (&xr)[8]) {
         int col[8];
         if constexpr (FUSED) {
             if (nO <= kIdxCap) {
@@ -377,13 +385,10 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             }
         } else {
             const __amdgpu_buffer_rsrc_t rI = make_rsrc(idx_g, 4 * K);
-            uint32_t ioff_hi = active ? 0u : 0x80000000u;   // (as for the data loads below)
-            asm volatile("" : "+v"(ioff_hi));
 #pragma unroll
             for (int e = 0; e < 8; e++)
                 col[e] = min(max((int)__builtin_amdgcn_raw_buffer_load_b32(
-                                     rI, (int)((uint32_t)(i0 + e < nO ? 4 * (i0 + e) : kOutOfRange) | ioff_hi),
-                                     0, 0),
+                                     rI, i0 + e < nO ? 4 * (i0 + e) : kOutOfRange, 0, 0),
                                  0),
                              K - 1);
         }
@@ -396,10 +401,6 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
                  : make_rsrc(Wq + (int64_t)rgc * kDRows * K, rows * K);
         const int ttok = min(tok, T - 1);
         const __amdgpu_buffer_rsrc_t rXg = FUSED ? make_rsrc(X, 2 * T * K) : make_rsrc(XO_g, 2 * T * K);
-        // bit 31 set in every offset of an inactive wave (past any buffer);
-        // opaque to the compiler, which would otherwise branch on `active`
-        uint32_t off_hi = active ? 0u : 0x80000000u;
-        asm volatile("" : "+v"(off_hi));
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             const bool ok = i0 + e < nO;
@@ -411,8 +412,8 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
                 const int i = i0 + e;
                 xo = ((i >> 4) * T + ttok) * 16 + (i & 15);
             }
-            const int woff = (int)((uint32_t)(ok ? (F16W ? 2 * wo : wo) : kOutOfRange) | off_hi);
-            const int xoff = (int)((uint32_t)(ok ? 2 * xo : kOutOfRange) | off_hi);
+            const int woff = ok ? (F16W ? 2 * wo : wo) : kOutOfRange;
+            const int xoff = ok ? 2 * xo : kOutOfRange;
             if constexpr (F16W)
                 wr[e] = __builtin_amdgcn_raw_buffer_load_b16(rWg, woff, 0, 0);
             else
@@ -433,26 +434,49 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     };
 
     auto process = [&](int set, int rgc, int par) {
-        // wave 0 requests its feature scales first, so that they arrive
-        // during the MFMAs
+        // The epilogue's small operands for this row group, spread over all
+        // 512 threads and requested before the MFMAs (loads complete in
+        // order: the MFMAs wait only for the older weight loads): thread
+        // (r = tid / 32, e = tid % 32) fetches the weight of row r and the
+        // activation of token slot r at outlier rank e, threads 0..15 the
+        // column scales.  Unconditional buffer loads (zeros past the ends);
+        // they go to LDS after the MFMAs, for wave 0 to read after the
+        // reduction barrier.
         const int nb = rgc * kDRows + 4 * kg;   // this lane's first feature
-        float swv[4];
+        uint32_t g_w, g_x, g_s;
         {
-            const __amdgpu_buffer_rsrc_t rS = make_rsrc(sW, 4 * N);
-            uint32_t soff_hi = wid == 0 ? 0u : 0x80000000u;   // (see gather_raw)
-            asm volatile("" : "+v"(soff_hi));
-#pragma unroll
-            for (int r = 0; r < 4; r++)
-                swv[r] = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(
-                               rS, (int)((uint32_t)(4 * min(nb + r, N - 1)) | soff_hi), 0, 0));
+            const int e = tid & 31, r = tid >> 5;
+            int col = 0;
+            if constexpr (FUSED) {
+                if (nO <= kIdxCap) {
+                    col = idxl[min(e, kIdxCap - 1)];
+                } else {   // more columns than the LDS list holds
+                    int c8[8];
+                    outlier_columns8(bits, pre, (K + 31) / 32, nO, e, c8);
+                    col = max(c8[0], 0);
+                }
+            } else {
+                col = min(max(g_idx, 0), K - 1);
+            }
+            const int rows = min(kDRows, N - rgc * kDRows);
+            const __amdgpu_buffer_rsrc_t rWg =
+                F16W ? make_rsrc(W16 + (int64_t)rgc * kDRows * K, 2 * rows * K)
+                     : make_rsrc(Wq + (int64_t)rgc * kDRows * K, rows * K);
+            const int wo = r * K + col;
+            const int woff = (e < nO && r < rows) ? (F16W ? 2 * wo : wo) : kOutOfRange;
+            if constexpr (F16W)
+                g_w = __builtin_amdgcn_raw_buffer_load_b16(rWg, woff, 0, 0);
+            else
+                g_w = __builtin_amdgcn_raw_buffer_load_b8(rWg, woff, 0, 0);   // (code byte)
+            // 16-column chunks of XO: rank i of token t at ((i / 16) * T + t) * 16 + i % 16
+            const int xo = FUSED ? r * K + col : ((e >> 4) * T + r) * 16 + (e & 15);
+            const __amdgpu_buffer_rsrc_t rXg = FUSED ? make_rsrc(X, 2 * T * K) : make_rsrc(XO_g, 2 * T * K);
+            g_x = __builtin_amdgcn_raw_buffer_load_b16(rXg, (e < nO && r < T) ? 2 * xo : kOutOfRange, 0, 0);
+            g_s = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(sW, 4 * N),
+                                                       tid < kDRows ? 4 * min(rgc * kDRows + tid, N - 1)
+                                                                    : kOutOfRange,
+                                                       0, 0);
         }
-        // wave 0 requests the first 32 outlier columns before its MFMAs
-        // (loads complete in order; the MFMAs wait only for the older
-        // weight loads)
-        int wr0[8];
-        uint32_t xr0[8];
-        gather_raw(rgc, 8 * kg, wid == 0, wr0, xr0);
         // fragment reads 8 at a time ahead of their MFMAs, which alternate
         // between two accumulators (the int32 sums are exact, so splitting
         // the dependency chain changes nothing)
@@ -473,11 +497,21 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
                 acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbuf[set][h + j + 1], xf[j + 1], acc2, 0, 0, 0);
             }
         }
+        // (no scheduling across: the stores below wait for the gathers)
+        __builtin_amdgcn_sched_barrier(0);
         acc += acc2;
+        gwl[tid] = (uint16_t)g_w;   // [r][e] = tid
+        gxl[tid] = (uint16_t)g_x;
+        if (tid < kDRows)
+            gsl[tid] = __builtin_bit_cast(float, g_s);
         red[(par * kDWaves + wid) * 64 + lane] = acc;
         lds_barrier();
         if (wid != 0)
             return;
+        float swv[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            swv[r] = gsl[4 * kg + r];
         // wave 0: lane holds token tok and features nb .. nb+3
         v4i tot = red[par * kDWaves * 64 + lane];
 #pragma unroll
@@ -505,12 +539,20 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         for (int c = 0; c < (nO + 31) / 32; c++) {
             const int i0 = 32 * c + 8 * kg;
             v8h a, b;
-            if (c == 0) {
+            if (c == 0) {   // from the LDS copies: weight row lane % 16, token slot tok
+                int wr0[8];
+                uint32_t xr0[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const uint16_t w = gwl[(lane & 15) * 32 + i0 + e];
+                    wr0[e] = F16W ? (int)w : (int)(int8_t)(w & 0xffu);
+                    xr0[e] = gxl[tok * 32 + i0 + e];
+                }
                 fragments(i0, wr0, xr0, a, b);
             } else {
                 int wr[8];
                 uint32_t xr[8];
-                gather_raw(rgc, i0, true, wr, xr);
+                gather_raw(rgc, i0, wr, xr);
                 fragments(i0, wr, xr, a, b);
             }
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, d, 0, 0, 0);
