@@ -58,8 +58,8 @@ constexpr int kOffBits = kXqMax;                          // uint32[K/32]
 constexpr int kOffPre = kOffBits + 4 * (kDMaxK / 32);     // int32[K/32]
 constexpr int kOffRmax = kOffPre + 4 * (kDMaxK / 32);     // uint32[8][16]
 constexpr int kOffSx = kOffRmax + 4 * kDWaves * kDMaxT;   // float[16] token scales
-constexpr int kOffRx = kOffSx + 4 * kDMaxT;               // float[16] their reciprocals
-constexpr int kOffRed = kOffRx + 4 * kDMaxT;              // v4i[2][8][64]
+constexpr int kOffZero = kOffSx + 4 * kDMaxT;             // 16 zero bytes (padding fragments)
+constexpr int kOffRed = kOffZero + 4 * kDMaxT;            // v4i[2][8][64]
 constexpr int kIdxCap = 512;                              // outlier columns listed in LDS
 constexpr int kOffIdx = kOffRed + 2 * kDWaves * 64 * 16;  // int32[kIdxCap]
 constexpr int kMaxCpt = kDMaxK / (8 * kDThreads);         // 8-column chunks per thread
@@ -135,7 +135,6 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     int32_t *pre = reinterpret_cast<int32_t *>(lds + kOffPre);
     uint32_t *rmax = reinterpret_cast<uint32_t *>(lds + kOffRmax);
     float *sxl = reinterpret_cast<float *>(lds + kOffSx);
-    float *rxl = reinterpret_cast<float *>(lds + kOffRx);
     int32_t *idxl = reinterpret_cast<int32_t *>(lds + kOffIdx);
     int32_t *ocnt = reinterpret_cast<int32_t *>(lds + kOffOcnt);
     uint16_t *gwl = reinterpret_cast<uint16_t *>(lds + kOffGw);
@@ -144,6 +143,8 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     v4i *red = reinterpret_cast<v4i *>(lds + kOffRed);
 
     const int tid = threadIdx.x, lane = tid & 63;
+    if (tid < 4)   // read by the lanes whose fragment slot holds no token or no column
+        reinterpret_cast<uint32_t *>(lds + kOffZero)[tid] = 0u;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int QS = 16 * T + 16;
     const int NRG = (N + kDRows - 1) / kDRows;
@@ -261,23 +262,25 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             rmax[wid * kDMaxT + lane] = m;
         }
         lds_barrier();
-        // one thread per token: its scale and the reciprocal (IEEE
-        // divisions), shared through LDS
-        if (tid < kDMaxT) {
+        // Every wave derives the token scales itself, lane t for token t:
+        // the maximum over the waves' partial maxima, the scale and its
+        // reciprocal (IEEE divisions), broadcast across the wave; no second
+        // barrier.  Wave 0 keeps the scales in LDS for the epilogue.
+        float sx[TB], rx[TB];
+        {
             uint32_t m = 0;
 #pragma unroll
             for (int w = 0; w < kDWaves; w++)
-                m = max(m, tid < TB ? rmax[w * kDMaxT + tid] : 0u);
+                m = max(m, lane < TB ? rmax[w * kDMaxT + min(lane, TB - 1)] : 0u);
             const float sc = h2f(m) / 127.0f;
-            sxl[tid] = sc;
-            rxl[tid] = 1.0f / sc;
-        }
-        lds_barrier();
-        float sx[TB], rx[TB];
+            const float rc = 1.0f / sc;
+            if (wid == 0 && lane < kDMaxT)
+                sxl[lane] = sc;
 #pragma unroll
-        for (int t = 0; t < TB; t++) {
-            sx[t] = sxl[t];
-            rx[t] = rxl[t];
+            for (int t = 0; t < TB; t++) {
+                sx[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), t));
+                rx[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rc), t));
+            }
         }
         // nO and the rank of this thread's first outlier column in each pass
         nO = 0;
@@ -485,11 +488,10 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         for (int h = 0; h < KB; h += 8) {
             v4i xf[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
+            for (int j = 0; j < 8; j++) {   // (no token or no column: the zero bytes)
                 const int q = (s0 + h + j) * 4 + kg;
-                xf[j] = v4i{0, 0, 0, 0};
-                if (tok < T && s0 + h + j < s1 && 16 * q < K)
-                    xf[j] = *reinterpret_cast<const v4i *>(xq + q * QS + 16 * tok);
+                const bool ok = tok < T && s0 + h + j < s1 && 16 * q < K;
+                xf[j] = *reinterpret_cast<const v4i *>(lds + (ok ? q * QS + 16 * tok : kOffZero));
             }
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
@@ -542,11 +544,14 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             if (c == 0) {   // from the LDS copies: weight row lane % 16, token slot tok
                 int wr0[8];
                 uint32_t xr0[8];
+                const uint4 wv = *reinterpret_cast<const uint4 *>(gwl + (lane & 15) * 32 + i0);
+                const uint4 xv4 = *reinterpret_cast<const uint4 *>(gxl + tok * 32 + i0);
+                const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w}, xw[4] = {xv4.x, xv4.y, xv4.z, xv4.w};
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    const uint16_t w = gwl[(lane & 15) * 32 + i0 + e];
+                    const uint32_t w = (ww[e >> 1] >> (16 * (e & 1))) & 0xffffu;
                     wr0[e] = F16W ? (int)w : (int)(int8_t)(w & 0xffu);
-                    xr0[e] = gxl[tok * 32 + i0 + e];
+                    xr0[e] = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
                 }
                 fragments(i0, wr0, xr0, a, b);
             } else {
