@@ -537,29 +537,33 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
                 d[r] *= swv[r];
         // D += X[:, O] . Wq[:, O]^T, 32 outlier columns per MFMA: lane
         // supplies weight row (lane & 15) and token tok at ranks
-        // 32c + 8*kg .. +7
-        for (int c = 0; c < (nO + 31) / 32; c++) {
-            const int i0 = 32 * c + 8 * kg;
-            v8h a, b;
-            if (c == 0) {   // from the LDS copies: weight row lane % 16, token slot tok
-                int wr0[8];
-                uint32_t xr0[8];
-                const uint4 wv = *reinterpret_cast<const uint4 *>(gwl + (lane & 15) * 32 + i0);
-                const uint4 xv4 = *reinterpret_cast<const uint4 *>(gxl + tok * 32 + i0);
-                const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w}, xw[4] = {xv4.x, xv4.y, xv4.z, xv4.w};
+        // 32c + 8*kg .. +7.  Chunk 0 from the LDS copies, straight-line code
+        // for the common case of at most 32 outlier columns; later chunks
+        // gathered here.
+        if (nO > 0) {
+            const int i0 = 8 * kg;
+            int wr0[8];
+            uint32_t xr0[8];
+            const uint4 wv = *reinterpret_cast<const uint4 *>(gwl + (lane & 15) * 32 + i0);
+            const uint4 xv4 = *reinterpret_cast<const uint4 *>(gxl + tok * 32 + i0);
+            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w}, xw[4] = {xv4.x, xv4.y, xv4.z, xv4.w};
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const uint32_t w = (ww[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    wr0[e] = F16W ? (int)w : (int)(int8_t)(w & 0xffu);
-                    xr0[e] = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                }
-                fragments(i0, wr0, xr0, a, b);
-            } else {
-                int wr[8];
-                uint32_t xr[8];
-                gather_raw(rgc, i0, wr, xr);
-                fragments(i0, wr, xr, a, b);
+            for (int e = 0; e < 8; e++) {
+                const uint32_t w = (ww[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                wr0[e] = F16W ? (int)w : (int)(int8_t)(w & 0xffu);
+                xr0[e] = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
             }
+            v8h a, b;
+            fragments(i0, wr0, xr0, a, b);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, d, 0, 0, 0);
+        }
+        for (int c = 1; c < (nO + 31) / 32; c++) {
+            const int i0 = 32 * c + 8 * kg;
+            int wr[8];
+            uint32_t xr[8];
+            gather_raw(rgc, i0, wr, xr);
+            v8h a, b;
+            fragments(i0, wr, xr, a, b);
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, d, 0, 0, 0);
         }
         if (tok >= T)
