@@ -204,6 +204,23 @@ def test_outlier_count_at_gather_capacity(n_out):
     assert o["nO"] == n_out
 
 
+@pytest.mark.parametrize("n_out", [32, 33, 512, 513])
+def test_few_token_outlier_list_capacity(n_out):
+    """The few-token kernel lists up to 512 outlier columns in LDS and
+    gathers the first 32 with all threads; counts on either side of both
+    limits, spread over K with one in the last 16 columns."""
+    T, K, N = 8, 2048, 100
+    rng = np.random.default_rng(7000 + n_out)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    cols = np.sort(rng.choice(K - 16, n_out - 1, replace=False))
+    cols = np.append(cols, K - 3)
+    X[:, cols] = rng.choice([-1.0, 1.0], (T, n_out)) * rng.uniform(20, 60, (T, n_out))
+    X = X.astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = check_full(X, W, 6.0, f"few-token {n_out} outlier columns")
+    assert o["nO"] == n_out
+
+
 def test_many_outliers_13b_like():
     """Hundreds of outlier columns (token-sparse outliers as in the 13B
     workload, at a higher rate) on a reduced shape."""
