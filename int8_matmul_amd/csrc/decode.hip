@@ -26,7 +26,9 @@
 //    order does not matter).
 //  - Wave 0 finishes the row group: dequantization, the outlier product as
 //    v_mfma_f32_16x16x32_f16 over chunks of 32 outlier columns (gathered
-//    from X and Wq by column index), the column scale and the fp16 store.
+//    from X and Wq by column index: the first chunk and the column scales
+//    by all threads before the MFMAs, through LDS), the column scale and
+//    the fp16 store.
 // The variant FUSED = false reads the token codes, scales and outlier
 // columns that the prepare kernels left in the workspace instead of
 // deriving them; everything after that is the same code, so the two
