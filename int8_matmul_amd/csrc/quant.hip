@@ -214,7 +214,9 @@ __device__ int load_bits_and_scan(const uint32_t *__restrict__ bits_g, int nw,
 // ---------------------------------------------------------------------------
 
 // REG: the bit set fits in kBitsPerThread words per thread (K <= 8192).
-template <int ROWS, bool REG>
+// RREG: 16-byte chunks per thread and row kept in registers (2 when K <=
+// 4096, else 4; columns past RREG * 8 * 256 are read again from memory).
+template <int ROWS, bool REG, int RREG>
 __global__ __launch_bounds__(kThreads) void k_prepare(
     const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq,
     const uint16_t *__restrict__ W16, int T, int K, int N,
@@ -227,7 +229,6 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
     __shared__ int32_t scan[kThreads / 64];
     __shared__ uint32_t redr[ROWS][kThreads / 64];
     __shared__ int nnz_s, miss_s;
-    constexpr int RREG = 4;   // chunks per thread and row kept in registers
     const int nw = (K + 31) / 32;
     uint32_t *bits = smem;
     int32_t *pre = reinterpret_cast<int32_t *>(smem + nw);
@@ -554,7 +555,9 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
     const int64_t wblocks = (N + wrows - 1) / wrows;
     const size_t lds = 12 * (size_t)(nw > 0 ? nw : 1);   // bits, prefix, non-zero words
     const int64_t xblocks = (T + kPrepRows - 1) / kPrepRows;
-    auto kp = nw <= kBitsPerThread * kThreads ? k_prepare<kPrepRows, true> : k_prepare<kPrepRows, false>;
+    const bool reg = nw <= kBitsPerThread * kThreads, narrow = K / 8 <= 2 * kThreads;
+    auto kp = reg ? (narrow ? k_prepare<kPrepRows, true, 2> : k_prepare<kPrepRows, true, 4>)
+                  : (narrow ? k_prepare<kPrepRows, false, 2> : k_prepare<kPrepRows, false, 4>);
     auto launch = [&](auto KP) {
     hipLaunchKernelGGL(KP, dim3((unsigned)(xblocks + wblocks)), dim3(kThreads), lds, s, X, Wq,
                        W16, (int)T, (int)K, (int)N, wrows, bits, meta,
