@@ -1,4 +1,4 @@
-"""Calls captured in a HIP graph and replayed.
+"""Calls captured in a HIP graph and replayed, and calls on two streams.
 
 The calls allocate nothing given a workspace, never synchronize and clear
 their device state with kernels of their own (no memset nodes), so a
@@ -108,3 +108,33 @@ def test_smoothquant_in_a_graph(T, K, N):
     Y2 = torch.empty_like(Y)
     replay_and_check(lambda: li8.smoothquant_linear(X, s_inv, Wq, sW, out=Y, workspace=ws),
                      lambda: li8.smoothquant_linear(X2, s_inv, Wq, sW, out=Y2, workspace=ws), Y)
+
+
+@pytest.mark.parametrize("T,K,N", [(300, 1024, 520), (8, 4096, 300)])
+def test_two_streams_two_workspaces(T, K, N):
+    """Two calls in flight at once on two streams, each with its own
+    workspace (the contract for concurrent calls), give the eager results."""
+    print(f"case two streams {T}x{K}x{N}", flush=True)
+    X, X2, W = inputs(T, K, N, 14)
+    Wq, sW = li8.quantize_weight(W)
+    ref1 = li8.linear(X, Wq, sW, 6.0)
+    ref2 = li8.linear(X2, Wq, sW, 6.0)
+    torch.cuda.synchronize()
+    ws1, ws2 = li8.new_workspace(T, K, N, DEV), li8.new_workspace(T, K, N, DEV)
+    Y1 = torch.empty((T, N), dtype=torch.float16, device=DEV)
+    Y2 = torch.empty_like(Y1)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        Y1.zero_()
+        Y2.zero_()
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s1):
+            for _ in range(4):
+                li8.linear(X, Wq, sW, 6.0, out=Y1, workspace=ws1)
+        with torch.cuda.stream(s2):
+            for _ in range(4):
+                li8.linear(X2, Wq, sW, 6.0, out=Y2, workspace=ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(Y1.view(torch.int16), ref1.view(torch.int16))
+        assert torch.equal(Y2.view(torch.int16), ref2.view(torch.int16))
