@@ -58,7 +58,7 @@ constexpr int kOutOfRange = (int)0x80000000;   // buffer offset past any operand
 constexpr int kXqMax = kDMaxK / 16 * (16 * kDMaxT + 16);
 constexpr int kOffBits = kXqMax;                          // uint32[K/32]
 constexpr int kOffPre = kOffBits + 4 * (kDMaxK / 32);     // int32[K/32]
-constexpr int kOffRmax = kOffPre + 4 * (kDMaxK / 32);     // uint32[8][16]
+constexpr int kOffRmax = kOffPre + 4 * (kDMaxK / 32);     // uint32[16][8]: token-major wave maxima
 constexpr int kOffSx = kOffRmax + 4 * kDWaves * kDMaxT;   // float[16] token scales
 constexpr int kOffZero = kOffSx + 4 * kDMaxT;             // 16 zero bytes (padding fragments)
 constexpr int kOffRed = kOffZero + 4 * kDMaxT;            // v4i[2][8][64]
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
 #pragma unroll
             for (int t = 1; t < TB; t++)
                 m = (lane == t) ? wm[t] : m;
-            rmax[wid * kDMaxT + lane] = m;
+            rmax[lane * kDWaves + wid] = m;
         }
         lds_barrier();
         // Every wave derives the token scales itself, lane t for token t:
@@ -270,10 +270,12 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // barrier.  Wave 0 keeps the scales in LDS for the epilogue.
         float sx[TB], rx[TB];
         {
-            uint32_t m = 0;
-#pragma unroll
-            for (int w = 0; w < kDWaves; w++)
-                m = max(m, lane < TB ? rmax[w * kDMaxT + min(lane, TB - 1)] : 0u);
+            // the 8 wave maxima of token min(lane, TB - 1) in two 16-byte
+            // reads (unconditional: a masked read is a branch per read)
+            const uint4 m0 = *reinterpret_cast<const uint4 *>(rmax + min(lane, TB - 1) * kDWaves);
+            const uint4 m1 = *reinterpret_cast<const uint4 *>(rmax + min(lane, TB - 1) * kDWaves + 4);
+            uint32_t m = max(max(max(m0.x, m0.y), max(m0.z, m0.w)), max(max(m1.x, m1.y), max(m1.z, m1.w)));
+            m = lane < TB ? m : 0u;
             const float sc = h2f(m) / 127.0f;
             const float rc = 1.0f / sc;
             if (wid == 0 && lane < kDMaxT)
