@@ -274,16 +274,26 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
     const int nO16 = (nO + 15) & ~15;   // <= K since K % 16 == 0
 
     if (xblock) {
+        // this thread's bit-set words, skip masks and word ranks, read once
+        // for all its rows and unconditionally (a clamped index; chunks
+        // past K hold zeros and store nothing): a read under the lane test
+        // would be a branch per read
+        uint32_t wbits[RREG], skipm[RREG];
+        int wpre[RREG];
+#pragma unroll
+        for (int s = 0; s < RREG; s++) {
+            const int c = tid + s * kThreads, wi = min(c, nchunk - 1) >> 2;
+            wbits[s] = bits[wi];
+            wpre[s] = pre[wi];
+            skipm[s] = (wbits[s] >> (8 * (c & 3))) & 0xffu;
+        }
         uint32_t m[ROWS];
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
             m[r] = 0;
 #pragma unroll
-            for (int s = 0; s < RREG; s++) {
-                const int c = tid + s * kThreads;
-                if (c < nchunk)
-                    m[r] = max(m[r], chunk_max(v[r][s], (bits[c >> 2] >> (8 * (c & 3))) & 0xffu));
-            }
+            for (int s = 0; s < RREG; s++)
+                m[r] = max(m[r], chunk_max(v[r][s], skipm[s]));
             const uint4 *xr = reinterpret_cast<const uint4 *>(X + (int64_t)min(t0 + r, T - 1) * K);
             for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads)
                 m[r] = max(m[r], chunk_max(xr[c], (bits[c >> 2] >> (8 * (c & 3))) & 0xffu));
@@ -320,14 +330,12 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
             // outlier values in 16-column chunks: rank i of row t at
             // ((i / 16) * T + t) * 16 + i % 16
             auto xo = [&](int i) -> uint16_t & { return XO[((int64_t)(i >> 4) * T + t) * 16 + (i & 15)]; };
-            auto emit = [&](int c, uint4 x) {
-                const uint32_t wbits = bits[c >> 2];
-                const uint32_t skip = (wbits >> (8 * (c & 3))) & 0xffu;
+            auto emit = [&](int c, uint4 x, uint32_t wb, uint32_t skip, int wp) {
                 q[c] = (sc == 0.0f) ? make_uint2(0u, 0u) : token_codes8(x, skip, sc, rc);
                 if (skip) {
                     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
                     const int b0 = 8 * (c & 3);
-                    int i = pre[c >> 2] + __popc(wbits & ((1u << b0) - 1u));
+                    int i = wp + __popc(wb & ((1u << b0) - 1u));
 #pragma unroll
                     for (int e = 0; e < 8; e++)
                         if ((skip >> e) & 1u)
@@ -338,11 +346,13 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
             for (int s2 = 0; s2 < RREG; s2++) {
                 const int c = tid + s2 * kThreads;
                 if (c < nchunk)
-                    emit(c, v[r][s2]);
+                    emit(c, v[r][s2], wbits[s2], skipm[s2], wpre[s2]);
             }
             const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
-            for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads)
-                emit(c, xr[c]);
+            for (int c = tid + RREG * kThreads; c < nchunk; c += kThreads) {
+                const uint32_t wb = bits[c >> 2];
+                emit(c, xr[c], wb, (wb >> (8 * (c & 3))) & 0xffu, pre[c >> 2]);
+            }
             if (tid < nO16 - nO)
                 xo(nO + tid) = 0;
         }
