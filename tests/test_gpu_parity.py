@@ -331,6 +331,21 @@ def test_large_tile_ragged_sampled():
     assert e <= TOL, f"fp16 output error {e}"
 
 
+def test_many_tokens_narrow():
+    """A token count far past one grid round of every kernel (the detection
+    grid's rows per workgroup, 65538 quantization workgroups, 512 row tiles
+    of the GEMM) on a narrow layer, checked in full against the oracle."""
+    T, K, N = 131072, 32, 48
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    X[:, 5] = rng.choice([-1.0, 1.0], T) * rng.uniform(20, 60, T)   # one fixed outlier column
+    X[T - 1, 30] = np.float32(40.0)                                   # and one in the last row only
+    X = X.astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = check_full(X, W, 6.0, "many tokens, narrow layer")
+    assert o["nO"] == 2
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, sampled rows
 # ---------------------------------------------------------------------------
