@@ -543,22 +543,25 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // supplies weight row (lane & 15) and token tok at ranks
         // 32c + 8*kg .. +7.  Chunk 0 from the LDS copies, straight-line code
         // for the common case of at most 32 outlier columns; later chunks
-        // gathered here.
-        if (nO > 0) {
+        // gathered here.  The copies hold zeros past rank nO and past token
+        // T, so chunk 0 needs no masks, and with no outlier columns at all
+        // it adds exact zeros (d is never -0: its integer part is not -0 and
+        // the scales are not negative).
+        {
             const int i0 = 8 * kg;
-            int wr0[8];
-            uint32_t xr0[8];
             const uint4 wv = *reinterpret_cast<const uint4 *>(gwl + (lane & 15) * 32 + i0);
             const uint4 xv4 = *reinterpret_cast<const uint4 *>(gxl + tok * 32 + i0);
             const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w}, xw[4] = {xv4.x, xv4.y, xv4.z, xv4.w};
+            v8h a, b;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                const uint32_t w = (ww[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                wr0[e] = F16W ? (int)w : (int)(int8_t)(w & 0xffu);
-                xr0[e] = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                const uint16_t w = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+                if constexpr (F16W)
+                    a[e] = __builtin_bit_cast(_Float16, w);
+                else
+                    a[e] = (_Float16)(float)(int8_t)(w & 0xffu);
+                b[e] = __builtin_bit_cast(_Float16, (uint16_t)(xw[e >> 1] >> (16 * (e & 1))));
             }
-            v8h a, b;
-            fragments(i0, wr0, xr0, a, b);
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, d, 0, 0, 0);
         }
         for (int c = 1; c < (nO + 31) / 32; c++) {
