@@ -574,14 +574,17 @@ hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, i
 
 } // namespace
 
-// Tile shape: 256x256 by default; 256x128 (8 waves of 64x64) when the
-// 256x256 grid leaves a large part of the last round of workgroups empty
-// (few tokens per 256 rows, or a tile count just above a multiple of the
-// CU count).  Cost model: rounds of workgroups over the 256 CUs times the
-// work of one tile, the smaller tile charged 35 % more per operation: its
-// lower reuse costs cycles and, under the power-limited clock of calls
-// back to back, energy (at 2048 x 4096 x 11008 the 256x256 grid's 1.34
-// rounds beat the 256x128 grid's 2.69 in whole calls).
+// Tile shape: 256x256 by default; 256x192 (8 waves of 64x96) or 256x128
+// (8 waves of 64x64) when the 256x256 grid leaves a large part of the last
+// round of workgroups empty (few tokens per 256 rows, or a tile count just
+// above a multiple of the CU count).  Cost model: rounds of workgroups over
+// the 256 CUs times the work of one tile, the smaller tiles charged 15 %
+// and 35 % more per operation: their lower reuse costs cycles and, under
+// the power-limited clock of calls back to back, energy.  (Measured: at
+// 2048 x 4096 x 11008 the 256x192 grid's 1.81 rounds beat the 256x256
+// grid's 1.34 and the 256x128 grid's 2.69; at 4096 x 4096 x 11008 the
+// 256x256 grid's 2.69 rounds beat the 256x192 grid's 3.63; at
+// 512 x 5120 x 13824 one round of 256x128 tiles beats both.)
 constexpr int kCUs = 256;
 
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
@@ -589,12 +592,17 @@ hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, 
                        hipStream_t s, const int8_t *WO)
 {
     const int64_t tm = (T + 255) / 256;
-    const int64_t big = tm * ((N + 255) / 256), small = tm * ((N + 127) / 128);
+    const int64_t big = tm * ((N + 255) / 256), mid = tm * ((N + 191) / 192),
+                  small = tm * ((N + 127) / 128);
     const double cost_big = (double)((big + kCUs - 1) / kCUs);
+    const double cost_mid = 0.75 * 1.15 * (double)((mid + kCUs - 1) / kCUs);
     const double cost_small = 0.5 * 1.35 * (double)((small + kCUs - 1) / kCUs);
-    if (cost_small < cost_big)
+    if (cost_small < cost_big && cost_small <= cost_mid)
         return fp16w ? launch_cfg<256, 128, 128, 2, 4, 2, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO)
                      : launch_cfg<256, 128, 128, 2, 4, 2, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO);
+    if (cost_mid < cost_big)
+        return fp16w ? launch_cfg<256, 192, 128, 2, 4, 2, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO)
+                     : launch_cfg<256, 192, 128, 2, 4, 2, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO);
     return fp16w ? launch_cfg<256, 256, 128, 2, 2, 4, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO)
                  : launch_cfg<256, 256, 128, 2, 2, 4, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO);
 }

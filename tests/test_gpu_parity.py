@@ -331,6 +331,39 @@ def test_large_tile_ragged_sampled():
     assert e <= TOL, f"fp16 output error {e}"
 
 
+def test_mid_tile_ragged_sampled():
+    """Ragged T and N where 256x128 tiles would need a second round and
+    256x256 tiles would leave a third of the round empty, so the library
+    takes 256x192 tiles (4 x 44, the last 64 features wide): int8 and
+    fp16-weight outlier products on sampled rows, accumulators included."""
+    T, K, N = 1000, 272, 8320
+    w = workloads.WORKLOADS["prefill_7b_ffn_up"]
+    X, _ = workloads.make_activation(w, seed=7, T=T, K=K)
+    W = workloads.make_weight(w, seed=8, N=N, K=K)
+    say(f"case mid-tile ragged: T={T} K={K} N={N}")
+    Xd, Wd = dev(X), dev(W)
+    Wq, sW = li8.quantize_weight(Wd)
+    ws = li8.new_workspace(T, K, N, DEV)
+    Y = li8.linear(Xd, Wq, sW, 6.0, workspace=ws)
+    Yh = li8.linear_fp16w(Xd, Wq, sW, Wd, 6.0, workspace=ws)
+    li8.prepare(Xd, Wq, 6.0, ws)
+    acc = torch.empty((T, N), dtype=torch.int32, device=DEV)
+    Y2 = li8.gemm(Wq, sW, T, ws, acc=acc)
+    Wq_o, sW_o = oracle.quantize_weight(W)
+    rows = np.array([0, 1, 255, 256, 511, 767, 768, 998, 999])
+    Yo, idx, Xq_o, sX_o, acc_o = oracle.linear_rows(X, Wq_o, sW_o, 6.0, rows)
+    assert len(idx) > 0, "the case should have outlier columns"
+    rows_t = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(host(acc.index_select(0, rows_t)), acc_o)
+    yg = host(Y.index_select(0, rows_t))
+    assert np.array_equal(yg.view(np.uint16), host(Y2.index_select(0, rows_t)).view(np.uint16))
+    e = rel_err(yg, Yo)
+    assert e <= TOL, f"fp16 output error {e}"
+    Yho = oracle.linear_rows(X, Wq_o, sW_o, 6.0, rows, W16=W)[0]
+    e = rel_err(host(Yh.index_select(0, rows_t)), Yho)
+    assert e <= TOL, f"fp16-weight output error {e}"
+
+
 def test_many_tokens_narrow():
     """A token count far past one grid round of every kernel (the detection
     grid's rows per workgroup, 65538 quantization workgroups, 512 row tiles
