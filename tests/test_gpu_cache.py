@@ -62,6 +62,7 @@ def batches(T, K, N, sparse=0.0, seed=0):
     (300, 272, 520, 0.0),       # ragged tiles, a few fixed outlier columns
     (96, 2048, 384, 2e-3),      # hundreds of outlier columns spread over K
     (1000, 4096, 1100, 0.0),
+    (1000, 272, 8320, 0.0),     # 256x192 GEMM tiles, the last 64 features wide
 ])
 def test_sequence_hits_misses_and_bits(T, K, N, sparse):
     print(f"case cache sequence {T}x{K}x{N} sparse={sparse}", flush=True)

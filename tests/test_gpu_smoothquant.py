@@ -179,7 +179,7 @@ def test_smoothing_helps_on_outlier_activations():
     assert es < 0.5 * e0
 
 
-@pytest.mark.parametrize("name", ["prefill_7b_ffn_up_t4096", "decode_7b_attn"])
+@pytest.mark.parametrize("name", ["prefill_7b_ffn_up_t4096", "prefill_7b_ffn_up", "decode_7b_attn"])
 def test_full_size_sampled(name):
     """Full-size call; Y checked on sampled rows against the oracle."""
     w = workloads.WORKLOADS[name]
