@@ -219,15 +219,20 @@ li8_status llm_int8_gemm_cached(const int8_t *Wq, const float *sW, int64_t T, in
                                 hipStream_t stream);
 
 /*
- * SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1): instead of
- * splitting off the outlier columns, one factor s_j per input feature moves
- * their range from the activation to the weight through the exact rewrite
+ * SmoothQuant-style W8A8 (lowentro.cn "model quantization" notes, Q9 and
+ * Q10; hncyxsy.com/news/230290, section 5.1): instead of splitting off the
+ * outlier columns, one factor s_j per input feature moves their range from
+ * the activation to the weight through the exact rewrite
  * X . W^T = (X / s) . (W * s)^T; both sides are then quantized with the
  * absmax scheme above and multiplied in int8, with no floating-point part.
- * The section gives the factor's formula garbled; it is read here as
+ * The factor is
  *   s_j = ax_j^alpha / aw_j^(1 - alpha)
  * with ax_j = max_t |X_cal[t,j]| over a calibration batch of activations,
- * aw_j = max_n |W[n,j]|, and the migration strength alpha in [0, 1].
+ * aw_j = max_n |W[n,j]|, and the migration strength alpha in [0, 1].  (Q10
+ * prints a garbled product form whose alpha = 0 value is aw_j; the quotient
+ * is what makes its own description hold: alpha = 0.5 balances the smoothed
+ * ranges ax_j / s_j and aw_j * s_j, alpha = 1 gives s_j = ax_j, and
+ * alpha = 0 flattens the weight range to 1 with s_j = 1 / aw_j.)
  * Offline, once per layer: smoothquant_column_absmax (of the calibration
  * batch and of W), smoothquant_factors, smoothquant_quantize_weight.  Per
  * call: smoothquant_linear, or smoothquant_prepare + llm_int8_gemm.

@@ -1,5 +1,8 @@
-// SmoothQuant-style W8A8 on the same int8 GEMM, for gfx950
-// (hncyxsy.com/news/230290, section 5.1).
+// SmoothQuant-style W8A8 on the same int8 GEMM, for gfx950 (lowentro.cn
+// "model quantization" notes, Q9: the rewrite; Q10: the factor, whose
+// printed product form is garbled and is read as the quotient below, the
+// form under which alpha = 0.5 balances the two smoothed ranges and
+// alpha = 0 flattens the weight's; hncyxsy.com/news/230290, section 5.1).
 //
 // The rewrite x . W^T = (x / s) . (W * s)^T with one factor s_j per input
 // channel moves quantization difficulty from the activation to the weight;

@@ -232,7 +232,7 @@ def linear_rows(X, Wq, sW, threshold: float, rows, W16=None):
 
 
 # --------------------------------------------------------------------------
-# SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1): see oracle.c
+# SmoothQuant-style W8A8 (lowentro.cn notes, Q9-Q10; hncyxsy.com/news/230290, section 5.1): see oracle.c
 # --------------------------------------------------------------------------
 
 def column_absmax(X):

@@ -96,8 +96,8 @@ def linear(Xbits, Wq, sW, threshold: float, Wbits=None):
 
 
 def sq_linear(Xbits, Wbits, X_cal_bits, alpha: float):
-    """SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1), every
-    step in Python: per-channel factors from the calibration rows and the
+    """SmoothQuant-style W8A8 (lowentro.cn notes, Q9-Q10; hncyxsy.com/news/230290,
+    section 5.1), every step in Python: per-channel factors from the calibration rows and the
     weight, the smoothed weight and activation, absmax int8 on both, exact
     integer products.  Returns dict(s, Wq, sW, Xq, sX, acc, Y_bits)."""
     K = len(Wbits[0])

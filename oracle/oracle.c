@@ -311,16 +311,34 @@ int oracle_num_threads(void)
 }
 
 /*
- * SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1): the exact
- * rewrite x . W^T = (x / s) . (W * s)^T with one factor s_j per input
- * channel moves quantization difficulty from the activation to the weight;
- * then both are quantized to int8 with the same absmax scheme as above and
- * multiplied with no outlier decomposition.
+ * SmoothQuant-style W8A8.  The exact rewrite x . W^T = (x / s) . (W * s)^T
+ * (lowentro.cn "model quantization" notes, Q9; hncyxsy.com/news/230290,
+ * section 5.1) with one factor s_j per input channel moves quantization
+ * difficulty from the activation to the weight; then both are quantized to
+ * int8 with the same absmax scheme as above and multiplied with no outlier
+ * decomposition.
  *
- * Readings (the printed factor formula is garbled):
- *   s_j = ax_j^alpha / aw_j^(1-alpha), ax_j = max_t |X_cal[t,j]| over a
- *   calibration batch, aw_j = max_n |W[n,j]|; computed in fp64, rounded to
- *   fp32; s_j = 1 when ax_j or aw_j is 0 (the channel carries nothing).
+ * The factor (lowentro.cn notes, Q10).  Its formula line is garbled: it
+ * prints a product, max|X_j|^alpha * max|W_j|^(1-alpha), and from it the
+ * value max|W_j| at alpha = 0.  It is read here as the quotient
+ *   s_j = ax_j^alpha / aw_j^(1-alpha)
+ * because the same answer says what the factor has to achieve and only the
+ * quotient achieves it.  After the rewrite the channel's ranges are
+ * ax_j / s_j (activation) and aw_j * s_j (weight):
+ *   - alpha = 0.5 is to balance them: ax/s = aw*s  <=>  s = sqrt(ax / aw);
+ *   - alpha = 1 moves all of the activation's difficulty to the weight,
+ *     s = ax (the activation range becomes 1; both forms agree here);
+ *   - alpha = 0 moves all of the weight's difficulty to the activation, so
+ *     the weight range becomes 1: s = 1 / aw.  The product's s = aw would
+ *     instead square the weight's range, the opposite of what the answer
+ *     describes, so its printed alpha = 0 value is not taken.
+ * (hncyxsy.com section 5.1 calls alpha = 0 "no migration", which neither
+ * form gives; not taken either.)
+ *
+ * Other readings:
+ *   ax_j = max_t |X_cal[t,j]| over a calibration batch, aw_j = max_n
+ *   |W[n,j]|; s_j computed in fp64, rounded to fp32; s_j = 1 when ax_j or
+ *   aw_j is 0 (the channel carries nothing).
  *   W'[n,j] = fl32(W[n,j] * s_j), then the weight absmax quantization.
  *   X'[t,j] = fl32(X[t,j] * fl32(1 / s_j)), then the token absmax
  *   quantization over all columns; Y = fp16(fl32(fl32(acc * sX') * sW')).

@@ -1,7 +1,7 @@
 """Parity of the SmoothQuant-style W8A8 path (smoothquant_*) with the CPU oracle.
 
-hncyxsy.com/news/230290, section 5.1: per-channel factors s_j move the
-activation's range into the weight, X . W^T = (X / s) . (W * s)^T, and both
+lowentro.cn notes Q9-Q10 and hncyxsy.com/news/230290, section 5.1:
+per-channel factors s_j move the activation's range into the weight, X . W^T = (X / s) . (W * s)^T, and both
 sides are quantized with the absmax int8 scheme, with no outlier split.
 Bar: bit-exact column maxima, factors, reciprocals, codes, scales and int32
 accumulators; fp16 Y bit-exact too, since both sides compute

@@ -490,8 +490,8 @@ def test_fp16w_brute_force_agrees_bit_exactly(case):
 
 
 # --------------------------------------------------------------------------
-# SmoothQuant-style W8A8 (hncyxsy.com/news/230290, section 5.1): x.W^T =
-# (x/s).(W*s)^T with per-channel factors, then absmax int8 on both sides
+# SmoothQuant-style W8A8 (lowentro.cn notes, Q9-Q10; hncyxsy.com/news/230290,
+# section 5.1): x.W^T = (x/s).(W*s)^T with per-channel factors, then absmax int8 on both sides
 # --------------------------------------------------------------------------
 
 def _sq_full(X, W, alpha, X_cal=None):
@@ -520,7 +520,12 @@ def test_sq_uniform_power_of_two_factor_is_the_plain_int8_path():
 
 def test_sq_factors_closed_forms():
     """alpha = 1 gives s = ax, alpha = 0 gives s = 1/aw, alpha = 0.5 gives
-    sqrt(ax/aw); a channel whose activation or weight maximum is 0 keeps 1."""
+    sqrt(ax/aw); a channel whose activation or weight maximum is 0 keeps 1.
+    (lowentro.cn notes, Q10: alpha = 1 moves all of the activation's range
+    to the weight, alpha = 0 all of the weight's to the activation, 0.5
+    splits it evenly.  The printed product form would give aw at alpha = 0,
+    squaring the weight's range instead; the quotient is the reading that
+    matches the answer's description, so that is what this pins.)"""
     ax = np.array([8.0, 0.5, 0.0, 3.0, 100.0], np.float32)
     aw = np.array([0.5, 2.0, 1.0, 0.0, 0.04], np.float32)
     live = (ax > 0) & (aw > 0)
