@@ -81,11 +81,42 @@ li8_status int8_quantize_weight(const void *W, int64_t N, int64_t K,
                                 int8_t *Wq, float *sW, hipStream_t stream);
 
 /*
- * Bytes of device workspace that llm_int8_linear and llm_int8_prepare need
- * for this shape.  It covers the worst case, every column an outlier, so
- * the size never depends on the data.  Returns 0 if the shape is invalid.
+ * Bytes of device workspace that is enough for every entry point below that
+ * takes one, for this shape.  It covers the worst case, every column an
+ * outlier, so the size never depends on the data; it is sized for the
+ * fp16-weight variant, whose gathered outlier weight columns are fp16.
+ * The int8 and SmoothQuant-style entry points (llm_int8_linear, _prepare,
+ * _gemm, _*_cached, smoothquant_prepare, smoothquant_linear) accept a
+ * workspace of llm_int8_linear_workspace_bytes(T, K, N) bytes for shapes on
+ * the tiled path, about N*K bytes less.  Returns 0 if the shape is invalid.
  */
 size_t llm_int8_workspace_bytes(int64_t T, int64_t K, int64_t N);
+
+/*
+ * Bytes of device workspace that llm_int8_linear itself needs for this
+ * shape: 0 when the call takes the one fused few-token kernel (see
+ * llm_int8_plan), else the int8 layout (about 3*T*K + N*K bytes, the worst
+ * case of every column an outlier).  Returns 0 for an invalid shape too.
+ */
+size_t llm_int8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N);
+
+/*
+ * Which kernels a call of this shape runs (introspection for tests and
+ * benchmarks; nothing is enqueued):
+ *   *path    LI8_PATH_EMPTY      T == 0 or N == 0, nothing is launched;
+ *            LI8_PATH_FEW_TOKENS T <= 16 and 16 <= K <= 8192: llm_int8_linear
+ *                                is one fused kernel, and llm_int8_gemm a
+ *                                kernel of the same structure reading the
+ *                                prepared workspace; *tile_m = T,
+ *                                *tile_n = 16 output features per row group;
+ *            LI8_PATH_TILED      the prepare kernels and the tiled int8 MFMA
+ *                                GEMM with output tiles of *tile_m x *tile_n.
+ * Returns LI8_ERR_SHAPE for an invalid shape, LI8_ERR_INVALID_ARG for a
+ * null pointer.
+ */
+enum { LI8_PATH_EMPTY = 0, LI8_PATH_FEW_TOKENS = 1, LI8_PATH_TILED = 2 };
+li8_status llm_int8_plan(int64_t T, int64_t K, int64_t N, int32_t *path, int32_t *tile_m,
+                         int32_t *tile_n);
 
 /*
  * The whole layer: Y[T,N] = decomposed X[T,K] . W^T.
@@ -95,9 +126,11 @@ size_t llm_int8_workspace_bytes(int64_t T, int64_t K, int64_t N);
  *              pure vector-wise int8 product); 0 makes every column that has
  *              a non-zero value an outlier.
  *   Y          [T,N] fp16 out, fully overwritten; must not alias an input.
- *   workspace  device buffer of at least llm_int8_workspace_bytes(T,K,N)
+ *   workspace  device buffer of at least llm_int8_linear_workspace_bytes(T,K,N)
  *              bytes, owned by the caller; its contents on entry do not
  *              matter.  Two calls in flight at once need two workspaces.
+ *              On the few-token path (llm_int8_plan) none is used, and
+ *              NULL is accepted.
  * Equivalent to llm_int8_prepare followed by llm_int8_gemm on the same
  * stream and workspace.
  */

@@ -28,7 +28,8 @@ import torch
 
 __all__ = [
     "Int8MatmulError", "LibraryNotBuilt", "library_path", "load_library",
-    "quantize_weight", "workspace_bytes", "new_workspace", "linear", "prepare",
+    "quantize_weight", "workspace_bytes", "linear_workspace_bytes", "plan", "new_workspace",
+    "linear", "prepare",
     "gemm", "export_stages", "few_token_path", "linear_fp16w", "prepare_fp16w",
     "gemm_fp16w", "smoothquant_column_absmax", "smoothquant_factors",
     "smoothquant_quantize_weight", "smoothquant_prepare", "smoothquant_linear",
@@ -48,17 +49,6 @@ STATUS = {
     4: "LI8_ERR_WORKSPACE",
     5: "LI8_ERR_HIP",
 }
-
-
-# Shapes the library runs on its few-token path: ``linear`` is one fused
-# kernel there (kDecodeMaxT / kDecodeMaxK in csrc/li8_internal.h).
-FEW_TOKEN_MAX_T = 16
-FEW_TOKEN_MAX_K = 8192
-
-
-def few_token_path(T: int, K: int) -> bool:
-    """True if ``linear`` runs as the single fused few-token kernel for T x K."""
-    return 1 <= T <= FEW_TOKEN_MAX_T and 16 <= K <= FEW_TOKEN_MAX_K
 
 
 class Int8MatmulError(RuntimeError):
@@ -93,6 +83,10 @@ def load_library() -> ctypes.CDLL:
     L.int8_quantize_weight.argtypes = [vp, i64, i64, vp, vp, vp]
     L.llm_int8_workspace_bytes.restype = sz
     L.llm_int8_workspace_bytes.argtypes = [i64, i64, i64]
+    L.llm_int8_linear_workspace_bytes.restype = sz
+    L.llm_int8_linear_workspace_bytes.argtypes = [i64, i64, i64]
+    L.llm_int8_plan.restype = ctypes.c_int
+    L.llm_int8_plan.argtypes = [i64, i64, i64, vp, vp, vp]
     L.llm_int8_linear.restype = ctypes.c_int
     L.llm_int8_linear.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp, sz, vp]
     L.llm_int8_prepare.restype = ctypes.c_int
@@ -186,6 +180,27 @@ def new_workspace(T: int, K: int, N: int, device) -> torch.Tensor:
     return torch.empty(workspace_bytes(T, K, N), dtype=torch.uint8, device=device)
 
 
+def linear_workspace_bytes(T: int, K: int, N: int) -> int:
+    """Bytes llm_int8_linear needs for this shape (0 on the few-token path)."""
+    return int(load_library().llm_int8_linear_workspace_bytes(T, K, N))
+
+
+PATHS = {0: "empty", 1: "few_tokens", 2: "tiled"}
+
+
+def plan(T: int, K: int, N: int) -> dict:
+    """Which kernels a call of this shape runs: path and output tile."""
+    path, tm, tn = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check("llm_int8_plan", load_library().llm_int8_plan(T, K, N, ctypes.byref(path),
+                                                          ctypes.byref(tm), ctypes.byref(tn)))
+    return dict(path=PATHS[path.value], tile_m=tm.value, tile_n=tn.value)
+
+
+def few_token_path(T: int, K: int) -> bool:
+    """True if ``linear`` runs as the single fused few-token kernel for T x K."""
+    return plan(T, K, 1)["path"] == "few_tokens"
+
+
 def _ws(workspace, T, K, N, device):
     if workspace is None:
         workspace = new_workspace(T, K, N, device)
@@ -207,7 +222,10 @@ def linear(X: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, threshold: float
     if out is None:
         out = torch.empty((T, N), dtype=torch.float16, device=X.device)
     _require(out, torch.float16, "out", 2)
-    ws = _ws(workspace, T, K, N, X.device)
+    if workspace is None and linear_workspace_bytes(T, K, N) == 0:
+        ws = torch.empty(0, dtype=torch.uint8, device=X.device)   # the fused path uses none
+    else:
+        ws = _ws(workspace, T, K, N, X.device)
     _check("llm_int8_linear",
            L.llm_int8_linear(_ptr(X), _ptr(Wq), _ptr(sW), float(threshold), T, K, N,
                              _ptr(out), _ptr(ws), ws.numel(), _stream(X.device)))

@@ -61,8 +61,30 @@ uint16_t threshold_magnitude(float thr)
 
 li8_status from_hip(hipError_t e) { return e == hipSuccess ? LI8_OK : LI8_ERR_HIP; }
 
+// Workspace bytes an entry point needs: WIDE for the fp16-weight variant
+// (fp16 outlier weight columns), else the int8 layout.
+enum WsKind { WS_I8, WS_WIDE };
+
+size_t ws_need(int64_t T, int64_t K, int64_t N, WsKind kind)
+{
+    const WsLayout L = ws_layout(T, K, N);
+    return kind == WS_WIDE ? L.total : L.total_i8;
+}
+
+li8_status check_ws(const void *ws, size_t ws_bytes, size_t need)
+{
+    if (ws && misaligned(ws))
+        return LI8_ERR_ALIGN;
+    if (!ws || ws_bytes < need)
+        return LI8_ERR_WORKSPACE;
+    return LI8_OK;
+}
+
+// ws_optional: the call takes the one fused few-token kernel, which uses
+// no workspace (a null workspace is then accepted).
 li8_status check_linear_args(const void *X, const int8_t *Wq, float threshold, int64_t T,
-                             int64_t K, int64_t N, const void *ws, size_t ws_bytes)
+                             int64_t K, int64_t N, const void *ws, size_t ws_bytes,
+                             WsKind kind, bool ws_optional = false)
 {
     li8_status st = check_shape(T, K, N);
     if (st != LI8_OK)
@@ -75,13 +97,14 @@ li8_status check_linear_args(const void *X, const int8_t *Wq, float threshold, i
         return LI8_ERR_INVALID_ARG;
     if (misaligned(X) || misaligned(Wq))
         return LI8_ERR_ALIGN;
-    if (!ws || misaligned(ws) || ws_bytes < ws_layout(T, K, N).total)
-        return ws && misaligned(ws) ? LI8_ERR_ALIGN : LI8_ERR_WORKSPACE;
-    return LI8_OK;
+    if (ws_optional)
+        return (ws && misaligned(ws)) ? LI8_ERR_ALIGN : LI8_OK;
+    return check_ws(ws, ws_bytes, ws_need(T, K, N, kind));
 }
 
 li8_status check_gemm_args(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
-                           const void *Y, const int32_t *acc, const void *ws, size_t ws_bytes)
+                           const void *Y, const int32_t *acc, const void *ws, size_t ws_bytes,
+                           WsKind kind, bool ws_optional = false)
 {
     li8_status st = check_shape(T, K, N);
     if (st != LI8_OK)
@@ -92,9 +115,9 @@ li8_status check_gemm_args(const int8_t *Wq, const float *sW, int64_t T, int64_t
         return LI8_ERR_INVALID_ARG;
     if (misaligned(Wq) || misaligned(sW) || misaligned(Y) || (acc && misaligned(acc)))
         return LI8_ERR_ALIGN;
-    if (!ws || misaligned(ws) || ws_bytes < ws_layout(T, K, N).total)
-        return ws && misaligned(ws) ? LI8_ERR_ALIGN : LI8_ERR_WORKSPACE;
-    return LI8_OK;
+    if (ws_optional)
+        return (ws && misaligned(ws)) ? LI8_ERR_ALIGN : LI8_OK;
+    return check_ws(ws, ws_bytes, ws_need(T, K, N, kind));
 }
 
 // W16 null: the int8 path; else the fp16-weight variant.  cache: null, or
@@ -182,14 +205,46 @@ size_t llm_int8_workspace_bytes(int64_t T, int64_t K, int64_t N)
 {
     if (check_shape(T, K, N) != LI8_OK)
         return 0;
-    return ws_layout(T, K, N).total;
+    return ws_need(T, K, N, WS_WIDE);
+}
+
+size_t llm_int8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N)
+{
+    if (check_shape(T, K, N) != LI8_OK || T == 0 || N == 0 || decode_shape(T, K))
+        return 0;
+    return ws_need(T, K, N, WS_I8);
+}
+
+li8_status llm_int8_plan(int64_t T, int64_t K, int64_t N, int32_t *path, int32_t *tile_m,
+                         int32_t *tile_n)
+{
+    li8_status st = check_shape(T, K, N);
+    if (st != LI8_OK)
+        return st;
+    if (!path || !tile_m || !tile_n)
+        return LI8_ERR_INVALID_ARG;
+    if (T == 0 || N == 0) {
+        *path = LI8_PATH_EMPTY;
+        *tile_m = *tile_n = 0;
+    } else if (decode_shape(T, K)) {
+        *path = LI8_PATH_FEW_TOKENS;
+        *tile_m = (int32_t)T;
+        *tile_n = 16;
+    } else {
+        const GemmPlan p = gemm_plan(T, K, N);
+        *path = LI8_PATH_TILED;
+        *tile_m = p.bm;
+        *tile_n = p.bn;
+    }
+    return LI8_OK;
 }
 
 li8_status llm_int8_prepare(const void *X, const int8_t *Wq, float threshold, int64_t T,
                             int64_t K, int64_t N, void *workspace, size_t workspace_bytes,
                             hipStream_t stream)
 {
-    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    li8_status st =
+        check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes, WS_I8);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     const WsLayout L = ws_layout(T, K, N);
@@ -203,7 +258,7 @@ li8_status llm_int8_prepare_fp16w(const void *X, const void *W, float threshold,
                                   hipStream_t stream)
 {
     li8_status st = check_linear_args(X, static_cast<const int8_t *>(W), threshold, T, K, N,
-                                      workspace, workspace_bytes);
+                                      workspace, workspace_bytes, WS_WIDE);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     const WsLayout L = ws_layout(T, K, N);
@@ -216,7 +271,7 @@ li8_status llm_int8_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K
                          void *Y, int32_t *acc, const void *workspace, size_t workspace_bytes,
                          hipStream_t stream)
 {
-    li8_status st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes);
+    li8_status st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes, WS_I8);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     return gemm_common(Wq, sW, nullptr, T, K, N, Y, acc, workspace, stream);
@@ -226,7 +281,8 @@ li8_status llm_int8_gemm_fp16w(const int8_t *Wq, const float *sW, const void *W,
                                int64_t K, int64_t N, void *Y, int32_t *acc, const void *workspace,
                                size_t workspace_bytes, hipStream_t stream)
 {
-    li8_status st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes);
+    li8_status st =
+        check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes, WS_WIDE);
     if (st == LI8_OK && T > 0 && N > 0 && K > 0) {
         if (!W)
             st = LI8_ERR_INVALID_ARG;
@@ -243,9 +299,12 @@ li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW, flo
                            int64_t T, int64_t K, int64_t N, void *Y, void *workspace,
                            size_t workspace_bytes, hipStream_t stream)
 {
-    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    const bool fused = decode_shape(T, K);
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes,
+                                      WS_I8, fused);
     if (st == LI8_OK)
-        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes, WS_I8,
+                             fused);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     return linear_common(X, Wq, sW, nullptr, threshold, T, K, N, Y, workspace, stream);
@@ -255,9 +314,12 @@ li8_status llm_int8_linear_fp16w(const void *X, const int8_t *Wq, const float *s
                                  float threshold, int64_t T, int64_t K, int64_t N, void *Y,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    const bool fused = decode_shape(T, K);
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes,
+                                      WS_WIDE, fused);
     if (st == LI8_OK)
-        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes, WS_WIDE,
+                             fused);
     if (st == LI8_OK && T > 0 && N > 0 && K > 0) {
         if (!W)
             st = LI8_ERR_INVALID_ARG;
@@ -327,7 +389,7 @@ li8_status smoothquant_prepare(const void *X, const float *s_inv, int64_t T, int
 {
     // the threshold is unused here; 0 passes the check
     li8_status st = check_linear_args(X, reinterpret_cast<const int8_t *>(s_inv), 0.0f, T, K, N,
-                                      workspace, workspace_bytes);
+                                      workspace, workspace_bytes, WS_I8);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     return from_hip(launch_sq_prepare(static_cast<const uint16_t *>(X), s_inv, T, K,
@@ -339,9 +401,9 @@ li8_status smoothquant_linear(const void *X, const float *s_inv, const int8_t *W
                               void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     li8_status st = check_linear_args(X, reinterpret_cast<const int8_t *>(s_inv), 0.0f, T, K, N,
-                                      workspace, workspace_bytes);
+                                      workspace, workspace_bytes, WS_I8);
     if (st == LI8_OK)
-        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes, WS_I8);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     hipError_t e = launch_sq_prepare(static_cast<const uint16_t *>(X), s_inv, T, K,
@@ -373,7 +435,8 @@ li8_status llm_int8_prepare_cached(const void *X, const int8_t *Wq, float thresh
                                    int64_t K, int64_t N, void *workspace, size_t workspace_bytes,
                                    void *cache, size_t cache_bytes, hipStream_t stream)
 {
-    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    li8_status st =
+        check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes, WS_I8);
     if (st == LI8_OK && T > 0 && N > 0)
         st = check_cache(cache, cache_bytes, K, N);
     if (st != LI8_OK || T == 0 || N == 0)
@@ -392,7 +455,7 @@ li8_status llm_int8_gemm_cached(const int8_t *Wq, const float *sW, int64_t T, in
                                 size_t workspace_bytes, const void *cache, size_t cache_bytes,
                                 hipStream_t stream)
 {
-    li8_status st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes);
+    li8_status st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes, WS_I8);
     if (st == LI8_OK && T > 0 && N > 0)
         st = check_cache(cache, cache_bytes, K, N);
     if (st != LI8_OK || T == 0 || N == 0)
@@ -405,9 +468,12 @@ li8_status llm_int8_linear_cached(const void *X, const int8_t *Wq, const float *
                                   void *workspace, size_t workspace_bytes, void *cache,
                                   size_t cache_bytes, hipStream_t stream)
 {
-    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes);
+    const bool fused = decode_shape(T, K);
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes,
+                                      WS_I8, fused);
     if (st == LI8_OK)
-        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes);
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes, WS_I8,
+                             fused);
     if (st == LI8_OK && T > 0 && N > 0)
         st = check_cache(cache, cache_bytes, K, N);
     if (st != LI8_OK || T == 0 || N == 0)
@@ -433,7 +499,7 @@ li8_status llm_int8_export_stages(const void *workspace, size_t workspace_bytes,
     if (st != LI8_OK)
         return st;
     const WsLayout L = ws_layout(T, K, N);
-    if (!workspace || workspace_bytes < L.total)
+    if (!workspace || workspace_bytes < L.WO)   // (the stages end where WO starts)
         return LI8_ERR_WORKSPACE;
     const char *ws = static_cast<const char *>(workspace);
     struct {

@@ -62,16 +62,19 @@ constexpr int kOffRmax = kOffPre + 4 * (kDMaxK / 32);     // uint32[16][8]: toke
 constexpr int kOffSx = kOffRmax + 4 * kDWaves * kDMaxT;   // float[16] token scales
 constexpr int kOffZero = kOffSx + 4 * kDMaxT;             // 16 zero bytes (padding fragments)
 constexpr int kOffRed = kOffZero + 4 * kDMaxT;            // v4i[2][8][64]
-constexpr int kIdxCap = 512;                              // outlier columns listed in LDS
+constexpr int kIdxCap = 256;                              // outlier columns listed in LDS
 constexpr int kOffIdx = kOffRed + 2 * kDWaves * 64 * 16;  // int32[kIdxCap]
 constexpr int kMaxCpt = kDMaxK / (8 * kDThreads);         // 8-column chunks per thread
 constexpr int kOffOcnt = kOffIdx + 4 * kIdxCap;           // int32[kMaxCpt][8] outlier columns per wave
 // the first 32 outlier columns of the row group's 16 weight rows and of the
-// 16 token slots, and the group's 16 column scales, gathered by all threads
-constexpr int kOffGw = kOffOcnt + 4 * kMaxCpt * kDWaves;  // uint16[16][32] code bytes (or fp16 weights)
-constexpr int kOffGx = kOffGw + 2 * 16 * 32;              // uint16[16][32] fp16 activations
-constexpr int kOffGs = kOffGx + 2 * 16 * 32;              // float[16]
-constexpr int kLds = kOffGs + 4 * kDRows;
+// 16 token slots, and the group's 16 column scales, gathered by all threads;
+// two copies, alternating between row groups like the partial sums, since
+// the other waves write the next group's copy while wave 0 may still read
+// this one
+constexpr int kOffGw = kOffOcnt + 4 * kMaxCpt * kDWaves;  // uint16[2][16][32] code bytes (or fp16 weights)
+constexpr int kOffGx = kOffGw + 2 * 2 * 16 * 32;          // uint16[2][16][32] fp16 activations
+constexpr int kOffGs = kOffGx + 2 * 2 * 16 * 32;          // float[2][16]
+constexpr int kLds = kOffGs + 2 * 4 * kDRows;
 static_assert(kLds <= 160 * 1024, "LDS of one workgroup");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes)
@@ -506,10 +509,12 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // (no scheduling across: the stores below wait for the gathers)
         __builtin_amdgcn_sched_barrier(0);
         acc += acc2;
-        gwl[tid] = (uint16_t)g_w;   // [r][e] = tid
-        gxl[tid] = (uint16_t)g_x;
+        uint16_t *gw = gwl + par * 16 * 32, *gx = gxl + par * 16 * 32;
+        float *gs = gsl + par * kDRows;
+        gw[tid] = (uint16_t)g_w;   // [r][e] = tid
+        gx[tid] = (uint16_t)g_x;
         if (tid < kDRows)
-            gsl[tid] = __builtin_bit_cast(float, g_s);
+            gs[tid] = __builtin_bit_cast(float, g_s);
         red[(par * kDWaves + wid) * 64 + lane] = acc;
         lds_barrier();
         if (wid != 0)
@@ -517,7 +522,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         float swv[4];
 #pragma unroll
         for (int r = 0; r < 4; r++)
-            swv[r] = gsl[4 * kg + r];
+            swv[r] = gs[4 * kg + r];
         // wave 0: lane holds token tok and features nb .. nb+3
         v4i tot = red[par * kDWaves * 64 + lane];
 #pragma unroll
@@ -549,8 +554,8 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // the scales are not negative).
         {
             const int i0 = 8 * kg;
-            const uint4 wv = *reinterpret_cast<const uint4 *>(gwl + (lane & 15) * 32 + i0);
-            const uint4 xv4 = *reinterpret_cast<const uint4 *>(gxl + tok * 32 + i0);
+            const uint4 wv = *reinterpret_cast<const uint4 *>(gw + (lane & 15) * 32 + i0);
+            const uint4 xv4 = *reinterpret_cast<const uint4 *>(gx + tok * 32 + i0);
             const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w}, xw[4] = {xv4.x, xv4.y, xv4.z, xv4.w};
             v8h a, b;
 #pragma unroll

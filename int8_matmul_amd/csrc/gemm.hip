@@ -587,10 +587,9 @@ hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, i
 // 512 x 5120 x 13824 one round of 256x128 tiles beats both.)
 constexpr int kCUs = 256;
 
-hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
-                       uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, bool fp16w,
-                       hipStream_t s, const int8_t *WO)
+GemmPlan gemm_plan(int64_t T, int64_t K, int64_t N)
 {
+    (void)K;
     const int64_t tm = (T + 255) / 256;
     const int64_t big = tm * ((N + 255) / 256), mid = tm * ((N + 191) / 192),
                   small = tm * ((N + 127) / 128);
@@ -598,9 +597,21 @@ hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, 
     const double cost_mid = 0.75 * 1.15 * (double)((mid + kCUs - 1) / kCUs);
     const double cost_small = 0.5 * 1.35 * (double)((small + kCUs - 1) / kCUs);
     if (cost_small < cost_big && cost_small <= cost_mid)
+        return {256, 128};
+    if (cost_mid < cost_big)
+        return {256, 192};
+    return {256, 256};
+}
+
+hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
+                       uint16_t *Y, int32_t *acc, const char *ws, const WsLayout &L, bool fp16w,
+                       hipStream_t s, const int8_t *WO)
+{
+    const GemmPlan p = gemm_plan(T, K, N);
+    if (p.bn == 128)
         return fp16w ? launch_cfg<256, 128, 128, 2, 4, 2, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO)
                      : launch_cfg<256, 128, 128, 2, 4, 2, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO);
-    if (cost_mid < cost_big)
+    if (p.bn == 192)
         return fp16w ? launch_cfg<256, 192, 128, 2, 4, 2, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO)
                      : launch_cfg<256, 192, 128, 2, 4, 2, 4, false>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO);
     return fp16w ? launch_cfg<256, 256, 128, 2, 2, 4, 4, true>(Wq, sW, T, K, N, Y, acc, ws, L, s, WO)

@@ -36,8 +36,10 @@ constexpr int kDecodeMaxBlocks = 256;   // one workgroup per CU
 //   WO   : int8, N*K elements  likewise Wq[n, idx[i]] at ((i/16)*N + n)*16 +
 //                              i%16.  In the fp16-weight variant the same
 //                              region holds fp16 W[n, idx[i]] (2*N*K bytes)
+// total_i8 ends the layout after an int8 WO (the int8 and SmoothQuant-style
+// paths); total after an fp16 one (every entry point).
 struct WsLayout {
-    size_t bits, meta, idx, sX, Xq, XO, WO, total;
+    size_t bits, meta, idx, sX, Xq, XO, WO, total_i8, total;
 };
 
 inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
@@ -52,8 +54,9 @@ inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
     L.sX = off;   off = align_up(off + 4 * (size_t)(T ? T : 1), A);
     L.Xq = off;   off = align_up(off + (size_t)T * (size_t)K + 16, A);
     L.XO = off;   off = align_up(off + 2 * (size_t)T * (size_t)K + 16, A);
-    L.WO = off;   off = align_up(off + 2 * (size_t)N * (size_t)K + 16, A);
-    L.total = off;
+    L.WO = off;
+    L.total_i8 = align_up(off + (size_t)N * (size_t)K + 16, A);
+    L.total = align_up(off + 2 * (size_t)N * (size_t)K + 16, A);
     return L;
 }
 
@@ -90,6 +93,12 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
                           uint16_t thr_mag, int64_t T, int64_t K, int64_t N, char *ws,
                           const WsLayout &L, hipStream_t s, char *cache = nullptr);
 hipError_t launch_cache_reset(char *cache, hipStream_t s);
+
+// Tile shape of the tiled GEMM for a call of this shape (gemm.hip).
+struct GemmPlan {
+    int bm, bn;
+};
+GemmPlan gemm_plan(int64_t T, int64_t K, int64_t N);
 
 // Launcher (gemm.hip).
 // fp16w: the outlier product uses the fp16 weight columns that the prepare

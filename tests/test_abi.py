@@ -40,6 +40,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "li8_status_str", "int8_quantize_weight", "llm_int8_workspace_bytes",
+        "llm_int8_linear_workspace_bytes", "llm_int8_plan",
         "llm_int8_linear", "llm_int8_prepare", "llm_int8_gemm", "llm_int8_export_stages",
         "llm_int8_linear_fp16w", "llm_int8_prepare_fp16w", "llm_int8_gemm_fp16w",
         "smoothquant_column_absmax", "smoothquant_factors", "smoothquant_quantize_weight",
@@ -81,6 +82,32 @@ def test_workspace_bytes(lib):
     assert a % 256 == 0
 
 
+def test_linear_workspace_bytes(lib):
+    """llm_int8_linear needs no workspace on the few-token path, and the
+    int8 layout (no fp16 weight columns) on the tiled path."""
+    lw, ws = lib.llm_int8_linear_workspace_bytes, lib.llm_int8_workspace_bytes
+    assert lw(8, 4096, 11008) == 0 and lw(16, 8192, 28672) == 0 and lw(1, 16, 1) == 0
+    assert lw(0, 4096, 16) == 0 and lw(16, 17, 16) == 0
+    a = lw(4096, 4096, 11008)
+    assert 4096 * 4096 * 3 + 11008 * 4096 <= a < 4096 * 4096 * 3 + 11008 * 4096 + (1 << 20)
+    assert ws(4096, 4096, 11008) - a >= 11008 * 4096
+    assert lw(17, 4096, 64) > 0 and lw(8, 8208, 64) > 0   # past either few-token bound
+
+
+def test_plan(lib):
+    assert li8.plan(8, 4096, 4096) == dict(path="few_tokens", tile_m=8, tile_n=16)
+    assert li8.plan(0, 4096, 4096)["path"] == "empty"
+    p = li8.plan(4096, 4096, 11008)
+    assert p["path"] == "tiled" and p["tile_m"] == 256 and p["tile_n"] in (128, 192, 256)
+    assert li8.plan(17, 16, 16)["path"] == "tiled"
+    with pytest.raises(li8.Int8MatmulError):
+        li8.plan(16, 24, 16)
+    path = ctypes.c_int32()
+    assert lib.llm_int8_plan(4, 16, 4, ctypes.byref(path), None, ctypes.byref(path)) == INVALID
+    assert li8.few_token_path(16, 8192) and not li8.few_token_path(17, 8192)
+    assert not li8.few_token_path(16, 8208)
+
+
 def test_quantize_weight_validation(lib):
     f = lib.int8_quantize_weight
     assert f(P, 4, 17, P, P, None) == SHAPE
@@ -116,7 +143,13 @@ def test_linear_validation(lib):
     assert call(Y=MIS) == ALIGN
     assert call(ws=MIS) == ALIGN
     assert call(ws=None) == WORKSPACE
-    assert call(wsb=need - 1) == WORKSPACE
+    # the int8 path does not need the fp16-weight variant's larger layout
+    need8 = lib.llm_int8_linear_workspace_bytes(32, 64, 48)
+    assert 0 < need8 < need
+    assert call(wsb=need8 - 1) == WORKSPACE
+    # few tokens: no workspace needed, but a misaligned one is still refused
+    assert call(T=8, ws=MIS) == ALIGN
+    assert call(T=8, X=None, ws=None, wsb=0) == INVALID
     # empty calls are valid and enqueue nothing, whatever the pointers
     assert call(T=0, X=None, Y=None, ws=None, wsb=0) == OK
     assert call(N=0, Wq=None, sW=None, Y=None, ws=None, wsb=0) == OK
@@ -126,16 +159,21 @@ def test_linear_validation(lib):
 
 def test_prepare_and_gemm_validation(lib):
     need = lib.llm_int8_workspace_bytes(32, 64, 48)
+    need8 = lib.llm_int8_linear_workspace_bytes(32, 64, 48)
     p = lib.llm_int8_prepare
     assert p(None, P, 6.0, 32, 64, 48, P, need, None) == INVALID
     assert p(P, P, math.nan, 32, 64, 48, P, need, None) == INVALID
-    assert p(P, P, 6.0, 32, 64, 48, P, need - 256, None) == WORKSPACE
+    assert p(P, P, 6.0, 32, 64, 48, P, need8 - 1, None) == WORKSPACE
     assert p(P, P, 6.0, 32, 72, 48, P, need, None) == SHAPE
     g = lib.llm_int8_gemm
     assert g(P, P, 32, 64, 48, None, None, P, need, None) == INVALID
     assert g(P, P, 32, 64, 48, P2, MIS, P, need, None) == ALIGN
     assert g(P, P, 32, 64, 48, P2, None, P, 16, None) == WORKSPACE
+    assert g(P, P, 32, 64, 48, P2, None, P, need8 - 1, None) == WORKSPACE
     assert g(P, P, 0, 64, 48, None, None, None, 0, None) == OK
+    # the fp16-weight variant needs the wider layout
+    assert lib.llm_int8_gemm_fp16w(P, P, P, 32, 64, 48, P2, None, P, need - 1, None) == WORKSPACE
+    assert lib.llm_int8_prepare_fp16w(P, P, 6.0, 32, 64, 48, P, need - 1, None) == WORKSPACE
     e = lib.llm_int8_export_stages
     assert e(None, 0, 32, 64, 48, None, None, None, None, None, None, None) == WORKSPACE
     assert e(P, need, 32, 65, 48, None, None, None, None, None, None, None) == SHAPE
@@ -183,7 +221,8 @@ def test_smoothquant_validation(lib):
     p = lib.smoothquant_prepare
     assert p(P, None, 32, 64, 48, P, need, None) == INVALID
     assert p(P, MIS, 32, 64, 48, P, need, None) == ALIGN
-    assert p(P, P, 32, 64, 48, P, need - 1, None) == WORKSPACE
+    assert p(P, P, 32, 64, 48, P, lib.llm_int8_linear_workspace_bytes(32, 64, 48) - 1,
+             None) == WORKSPACE
     assert p(None, None, 0, 64, 48, None, 0, None) == OK
     L = lib.smoothquant_linear
     assert L(P, P, P, None, 32, 64, 48, P2, P, need, None) == INVALID   # no sW

@@ -6,8 +6,8 @@ max |Y_gpu - Y_oracle| / (1 + |Y_oracle|) <= 1e-2; with no outlier column
 the output is bit-exact as well (both sides compute
 fp16(fl32(fl32(acc * sX) * sW)) with no other term).
 
-Small shapes are compared element by element; the full-size workloads on
-sampled rows (the outlier set is computed by the oracle over all of X).
+Every case is compared element by element (the full-size workloads are in
+test_gpu_full_size.py).
 """
 import numpy as np
 import pytest
@@ -154,8 +154,8 @@ def test_ragged_shapes(T, K, N, thr):
     check_full(X, W, thr, f"ragged {T}x{K}x{N}")
 
 
-# T <= 16 and K <= 8192 take the few-token path (one fused kernel for
-# linear, a kernel reading the prepared workspace for gemm).
+# T <= 16: the few-token shapes, decode-time projections of 7B-70B layers
+# among them (the library's path for each is llm_int8_plan's choice).
 @pytest.mark.parametrize("T,K,N", [
     (1, 4096, 4101),     # one token; the last 16-feature row group holds 5 features
     (3, 48, 17),         # K not a multiple of 64: the last MFMA k-step is part padding
@@ -165,6 +165,11 @@ def test_ragged_shapes(T, K, N, thr):
     (16, 16, 33),        # one 16-column block of K
     (9, 2048, 100),      # the first T past the 8-token bound
     (8, 8192, 70),       # 8 tokens, two chunks of X per thread, the largest K
+    (8, 4096, 11008),    # 7B FFN up: 688 row groups, about three per workgroup
+    (16, 5120, 13824),   # 13B FFN up at 16 tokens: 864 row groups
+    (8, 11008, 4096),    # 7B FFN down: K past the few-token kernel's bound
+    (1, 13824, 512),     # 13B FFN down, one token
+    (16, 28672, 64),     # 70B FFN down width, 16 tokens
 ])
 @pytest.mark.parametrize("thr", [6.0, np.inf, 0.0])
 def test_decode_shapes(T, K, N, thr):
@@ -204,9 +209,9 @@ def test_outlier_count_at_gather_capacity(n_out):
     assert o["nO"] == n_out
 
 
-@pytest.mark.parametrize("n_out", [32, 33, 512, 513])
+@pytest.mark.parametrize("n_out", [32, 33, 256, 257, 513])
 def test_few_token_outlier_list_capacity(n_out):
-    """The few-token kernel lists up to 512 outlier columns in LDS and
+    """The few-token kernel lists up to 256 outlier columns in LDS and
     gathers the first 32 with all threads; counts on either side of both
     limits, spread over K with one in the last 16 columns."""
     T, K, N = 8, 2048, 100
@@ -304,63 +309,33 @@ def test_determinism_and_canary():
     assert np.all(host(buf[T * N:]) == sentinel)
 
 
-def test_large_tile_ragged_sampled():
-    """Ragged T and N where the 256x256 tiles fill exactly one round of
-    workgroups (so the library keeps them), checked on sampled rows,
-    accumulators included."""
-    T, K, N = 1000, 272, 16300
+@pytest.mark.parametrize("T,K,N,tile_n", [
+    (1000, 272, 16300, 256),   # 4 x 64 tiles of 256x256: exactly one round
+    (1000, 272, 8320, 192),    # 4 x 44 tiles of 256x192, the last 64 features wide
+    (300, 272, 520, 128),      # 2 x 5 tiles of 256x128
+])
+def test_tile_shapes_ragged(T, K, N, tile_n):
+    """Each output tile shape of the tiled GEMM on ragged T and N, every
+    element against the oracle (int8 path), and the fp16-weight variant's
+    output and accumulators on the same tiles."""
+    assert li8.plan(T, K, N) == dict(path="tiled", tile_m=256, tile_n=tile_n)
     w = workloads.WORKLOADS["prefill_7b_ffn_up"]
-    X, _ = workloads.make_activation(w, seed=5, T=T, K=K)
-    W = workloads.make_weight(w, seed=6, N=N, K=K)
-    say(f"case large-tile ragged: T={T} K={K} N={N}")
+    X, _ = workloads.make_activation(w, seed=5 + tile_n, T=T, K=K)
+    W = workloads.make_weight(w, seed=6 + tile_n, N=N, K=K)
+    g, o = check_full(X, W, 6.0, f"tile {tile_n}: {T}x{K}x{N}")
+    assert o["nO"] > 0, "the case should have outlier columns"
     Xd, Wd = dev(X), dev(W)
     Wq, sW = li8.quantize_weight(Wd)
     ws = li8.new_workspace(T, K, N, DEV)
-    Y = li8.linear(Xd, Wq, sW, 6.0, workspace=ws)
-    li8.prepare(Xd, Wq, 6.0, ws)
-    acc = torch.empty((T, N), dtype=torch.int32, device=DEV)
-    Y2 = li8.gemm(Wq, sW, T, ws, acc=acc)
-    Wq_o, sW_o = oracle.quantize_weight(W)
-    rows = np.array([0, 1, 255, 256, 511, 767, 768, 998, 999])
-    Yo, idx, Xq_o, sX_o, acc_o = oracle.linear_rows(X, Wq_o, sW_o, 6.0, rows)
-    rows_t = torch.from_numpy(rows).to(DEV)
-    assert np.array_equal(host(acc.index_select(0, rows_t)), acc_o)
-    yg = host(Y.index_select(0, rows_t))
-    assert np.array_equal(yg.view(np.uint16), host(Y2.index_select(0, rows_t)).view(np.uint16))
-    e = rel_err(yg, Yo)
-    assert e <= TOL, f"fp16 output error {e}"
-
-
-def test_mid_tile_ragged_sampled():
-    """Ragged T and N where 256x128 tiles would need a second round and
-    256x256 tiles would leave a third of the round empty, so the library
-    takes 256x192 tiles (4 x 44, the last 64 features wide): int8 and
-    fp16-weight outlier products on sampled rows, accumulators included."""
-    T, K, N = 1000, 272, 8320
-    w = workloads.WORKLOADS["prefill_7b_ffn_up"]
-    X, _ = workloads.make_activation(w, seed=7, T=T, K=K)
-    W = workloads.make_weight(w, seed=8, N=N, K=K)
-    say(f"case mid-tile ragged: T={T} K={K} N={N}")
-    Xd, Wd = dev(X), dev(W)
-    Wq, sW = li8.quantize_weight(Wd)
-    ws = li8.new_workspace(T, K, N, DEV)
-    Y = li8.linear(Xd, Wq, sW, 6.0, workspace=ws)
     Yh = li8.linear_fp16w(Xd, Wq, sW, Wd, 6.0, workspace=ws)
-    li8.prepare(Xd, Wq, 6.0, ws)
+    li8.prepare_fp16w(Xd, Wd, 6.0, ws)
     acc = torch.empty((T, N), dtype=torch.int32, device=DEV)
-    Y2 = li8.gemm(Wq, sW, T, ws, acc=acc)
-    Wq_o, sW_o = oracle.quantize_weight(W)
-    rows = np.array([0, 1, 255, 256, 511, 767, 768, 998, 999])
-    Yo, idx, Xq_o, sX_o, acc_o = oracle.linear_rows(X, Wq_o, sW_o, 6.0, rows)
-    assert len(idx) > 0, "the case should have outlier columns"
-    rows_t = torch.from_numpy(rows).to(DEV)
-    assert np.array_equal(host(acc.index_select(0, rows_t)), acc_o)
-    yg = host(Y.index_select(0, rows_t))
-    assert np.array_equal(yg.view(np.uint16), host(Y2.index_select(0, rows_t)).view(np.uint16))
-    e = rel_err(yg, Yo)
-    assert e <= TOL, f"fp16 output error {e}"
-    Yho = oracle.linear_rows(X, Wq_o, sW_o, 6.0, rows, W16=W)[0]
-    e = rel_err(host(Yh.index_select(0, rows_t)), Yho)
+    Yh2 = li8.gemm_fp16w(Wq, sW, Wd, T, ws, acc=acc)
+    oh = oracle.linear(X, g["Wq"], g["sW"], 6.0, stages=True, W16=W)
+    assert np.array_equal(host(acc), oh["acc"]), "fp16-weight accumulators"
+    yh = host(Yh)
+    assert np.array_equal(yh.view(np.uint16), host(Yh2).view(np.uint16))
+    e = rel_err(yh, oh["Y"])
     assert e <= TOL, f"fp16-weight output error {e}"
 
 
@@ -377,47 +352,3 @@ def test_many_tokens_narrow():
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
     g, o = check_full(X, W, 6.0, "many tokens, narrow layer")
     assert o["nO"] == 2
-
-
-# ---------------------------------------------------------------------------
-# full-size workloads, sampled rows
-# ---------------------------------------------------------------------------
-
-FULL = ["decode_7b_attn", "prefill_7b_ffn_up", "prefill_7b_ffn_up_t4096", "ffn_13b",
-        "ffn_70b_slice", "ffn_70b_slice_no_outliers"]
-
-
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
-    w = workloads.WORKLOADS[name]
-    say(f"case full {name}: T={w.T} K={w.K} N={w.N}")
-    X, W, cols = workloads.make(name)
-    T, K, N = w.T, w.K, w.N
-    Xd, Wd = dev(X), dev(W)
-    Wq, sW = li8.quantize_weight(Wd)
-    ws = li8.new_workspace(T, K, N, DEV)
-    Y = li8.linear(Xd, Wq, sW, w.threshold, workspace=ws)   # the call the benchmark times
-    li8.prepare(Xd, Wq, w.threshold, ws)   # the stages are defined by a prepare call
-    st = li8.export_stages(ws, T, K, N)
-    acc = torch.empty((T, N), dtype=torch.int32, device=DEV)
-    Y2 = li8.gemm(Wq, sW, T, ws, acc=acc)
-    Wq_o, sW_o = oracle.quantize_weight(W)
-    assert np.array_equal(host(sW), sW_o)
-    assert np.array_equal(host(Wq), Wq_o)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, T // 2, T - 1], rng.integers(0, T, 4)]))
-    Yo, idx, Xq_o, sX_o, acc_o = oracle.linear_rows(X, Wq_o, sW_o, w.threshold, rows)
-    nO = int(host(st["n_outliers"])[0])
-    assert nO == len(idx) and np.array_equal(host(st["outlier_idx"])[:nO], idx)
-    assert set(cols) <= set(idx)
-    rows_t = torch.from_numpy(rows).to(DEV)
-    assert np.array_equal(host(st["Xq"].index_select(0, rows_t)), Xq_o)
-    assert np.array_equal(host(st["sX"])[rows], sX_o)
-    assert np.array_equal(host(acc.index_select(0, rows_t)), acc_o)
-    yg = host(Y.index_select(0, rows_t))
-    assert np.array_equal(yg.view(np.uint16), host(Y2.index_select(0, rows_t)).view(np.uint16))
-    e = rel_err(yg, Yo)
-    assert e <= TOL, f"{name}: fp16 output error {e}"
-    if nO == 0:
-        assert_bit_exact(yg, Yo, acc_o, sX_o, sW_o)
-    say(f"  {name}: nO={nO} max rel err {e:.3e}")

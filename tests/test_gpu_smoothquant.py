@@ -177,28 +177,3 @@ def test_smoothing_helps_on_outlier_activations():
     es, e0 = np.abs(Ys - ref).mean(), np.abs(Y0 - ref).mean()
     print(f"mean |err|: smoothed {es:.4g}, plain absmax {e0:.4g}", flush=True)
     assert es < 0.5 * e0
-
-
-@pytest.mark.parametrize("name", ["prefill_7b_ffn_up_t4096", "prefill_7b_ffn_up", "decode_7b_attn"])
-def test_full_size_sampled(name):
-    """Full-size call; Y checked on sampled rows against the oracle."""
-    w = workloads.WORKLOADS[name]
-    print(f"case full sq {name}", flush=True)
-    Tcal = 256
-    Xall, _ = workloads.make_activation(w, T=w.T + Tcal)
-    X, Xcal = Xall[:w.T], Xall[w.T:]
-    W = workloads.make_weight(w)
-    s_o = oracle.sq_factors(oracle.column_absmax(Xcal), oracle.column_absmax(W), 0.5)
-    Wq_o, sW_o = oracle.sq_quantize_weight(W, s_o)
-    Wd = dev(W)
-    s_g, r_g = li8.smoothquant_factors(li8.smoothquant_column_absmax(dev(Xcal)),
-                                       li8.smoothquant_column_absmax(Wd), 0.5)
-    Wq, sW = li8.smoothquant_quantize_weight(Wd, s_g)
-    assert np.array_equal(bits(host(s_g)), bits(s_o))
-    assert np.array_equal(bits(host(sW)), bits(sW_o))
-    Y = li8.smoothquant_linear(dev(X), r_g, Wq, sW)
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, w.T - 1], rng.integers(0, w.T, 4)]))
-    o = oracle.sq_linear(X[rows], s_o, Wq_o, sW_o)
-    yg = host(Y.index_select(0, torch.from_numpy(rows).to(DEV)))
-    assert np.array_equal(bits(yg), bits(o))

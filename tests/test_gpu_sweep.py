@@ -10,8 +10,8 @@ against the oracle:
   llm_int8_linear_cached: Y bit-identical to llm_int8_linear on a miss and
     on the following hit;
   smoothquant_linear: Y bit-exact against the oracle's smoothed product.
-The shapes cover the tiled and the few-token paths and both tile shapes of
-the GEMM, with ragged edges everywhere.
+The shapes cover the tiled and the few-token paths and every output tile
+shape of the GEMM (asserted), with ragged edges everywhere.
 """
 import dataclasses
 
@@ -51,12 +51,23 @@ def rel_err(y, ref):
     return float(np.max(np.abs(y - ref) / (1.0 + np.abs(ref)))) if y.size else 0.0
 
 
+def draw_shape(rng, i):
+    """Every fourth case few tokens; every fourth (from 1) a wide layer of a
+    few hundred to a thousand tokens and 4000-17000 features at small K, so
+    that every output tile shape of the tiled GEMM is drawn; the rest small
+    and ragged."""
+    kind = i % 4
+    if kind == 0:
+        return int(rng.integers(1, 17)), 16 * int(rng.integers(1, 513)), int(rng.integers(1, 900))
+    if kind == 1:
+        T, N = int(rng.integers(257, 1101)), int(rng.integers(4000, 17001))
+        return T, 16 * int(rng.integers(1, 33)), N
+    return int(rng.integers(17, 700)), 16 * int(rng.integers(1, 200)), int(rng.integers(1, 900))
+
+
 def draw_case(i):
     rng = np.random.default_rng(1000 + i)
-    few = i % 4 == 0
-    T = int(rng.integers(1, 17)) if few else int(rng.integers(17, 700))
-    K = 16 * int(rng.integers(1, 513 if few else 200))
-    N = int(rng.integers(1, 900))
+    T, K, N = draw_shape(rng, i)
     thr = float(rng.choice([6.0, 6.0, 3.0, 20.0, np.inf, 0.0]))
     w = dataclasses.replace(workloads.WORKLOADS["ffn_13b"], T=T, K=K, N=N,
                             n_fixed=int(min(K, rng.integers(0, 12))),
@@ -64,6 +75,17 @@ def draw_case(i):
     X, _ = workloads.make_activation(w, seed=int(rng.integers(1 << 30)))
     W = workloads.make_weight(w, seed=int(rng.integers(1 << 30)))
     return T, K, N, thr, X, W
+
+
+def test_sweep_draws_every_path_and_tile():
+    """The sweep's shapes reach the few-token kernel and each tile shape of
+    the tiled GEMM (as the library itself plans them)."""
+    seen = set()
+    for i in range(CASES):
+        T, K, N = draw_shape(np.random.default_rng(1000 + i), i)
+        p = li8.plan(T, K, N)
+        seen.add((p["path"], p["tile_n"]))
+    assert {("few_tokens", 16), ("tiled", 128), ("tiled", 192), ("tiled", 256)} <= seen, seen
 
 
 @pytest.mark.parametrize("i", range(CASES))

@@ -76,6 +76,19 @@ WORKLOADS = {
         Workload("ffn_70b_slice_no_outliers", 4096, 8192, 28672, 0, 0.0, 0.0, 0.01,
                  no_outliers=True,
                  desc="70B-class FFN slice with no outlier columns"),
+        # Decode-time (few-token) FFN projections of the same model sizes:
+        # up-projections have many output features, down-projections a
+        # long K (the FFN width).  Same recipe as the attention projection.
+        Workload("decode_7b_ffn_up", 8, 4096, 11008, 4, 20.0, 100.0, 0.02,
+                 desc="decode-shaped 7B FFN up-projection, T=8 K=4096 N=11008"),
+        Workload("decode_7b_ffn_down", 8, 11008, 4096, 4, 20.0, 100.0, 0.02,
+                 desc="decode-shaped 7B FFN down-projection, T=8 K=11008 N=4096"),
+        Workload("decode_13b_ffn_up", 16, 5120, 13824, 8, 20.0, 100.0, 0.015,
+                 desc="decode-shaped 13B FFN up-projection, T=16 K=5120 N=13824"),
+        Workload("decode_13b_ffn_down", 1, 13824, 5120, 8, 20.0, 100.0, 0.015,
+                 desc="decode-shaped 13B FFN down-projection, one token, K=13824 N=5120"),
+        Workload("decode_70b_ffn_down", 16, 28672, 8192, 8, 20.0, 100.0, 0.01,
+                 desc="decode-shaped 70B FFN down-projection, T=16 K=28672 N=8192"),
     ]
 }
 
