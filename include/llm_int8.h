@@ -60,8 +60,10 @@ typedef enum li8_status {
                                 T*K or N*K >= 2^31                         */
     LI8_ERR_ALIGN = 3,       /* a pointer not 16-byte aligned               */
     LI8_ERR_WORKSPACE = 4,   /* workspace null or smaller than required     */
-    LI8_ERR_HIP = 5          /* a HIP launch or copy failed to enqueue (for
+    LI8_ERR_HIP = 5,         /* a HIP launch or copy failed to enqueue (for
                                 example: no gfx950 code for this device)   */
+    LI8_ERR_SCRATCH = 6      /* llm_int8_linear_noalloc: the shape needs more
+                                than its fixed scratch array               */
 } li8_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -138,6 +140,29 @@ li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW,
                            float threshold, int64_t T, int64_t K, int64_t N,
                            void *Y, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * llm_int8_linear for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same result bit for bit, with the
+ * workspace taken from a fixed array that the library holds on each GPU it
+ * runs on, LI8_NOALLOC_SCRATCH_BYTES bytes (128 MiB) for the life of the
+ * process.  Nothing is allocated or freed on any call.
+ *   - Arguments as for llm_int8_linear, without the workspace.
+ *   - Shapes whose workspace (llm_int8_linear_workspace_bytes) exceeds the
+ *     array return LI8_ERR_SCRATCH and enqueue nothing (4096 x 4096 x 11008
+ *     needs about 96 MB; few-token shapes need none).
+ *   - Every call on one GPU uses that GPU's one array, so calls that
+ *     overlap on one GPU (two streams, two host threads) race and give
+ *     wrong results: order them.  Nothing carries over from one call to
+ *     the next; each call clears what must start at zero.
+ *   - The first call on a device looks the array's address up (a host-side
+ *     query, no allocation); a failure there returns LI8_ERR_HIP.
+ */
+#define LI8_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+li8_status llm_int8_linear_noalloc(const void *X, const int8_t *Wq, const float *sW,
+                                   float threshold, int64_t T, int64_t K, int64_t N,
+                                   void *Y, hipStream_t stream);
 
 /*
  * First half of llm_int8_linear (steps 1-2 above): outlier detection,

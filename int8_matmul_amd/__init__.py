@@ -29,7 +29,7 @@ import torch
 __all__ = [
     "Int8MatmulError", "LibraryNotBuilt", "library_path", "load_library",
     "quantize_weight", "workspace_bytes", "linear_workspace_bytes", "plan", "new_workspace",
-    "linear", "prepare",
+    "linear", "linear_noalloc", "NOALLOC_SCRATCH_BYTES", "prepare",
     "gemm", "export_stages", "few_token_path", "linear_fp16w", "prepare_fp16w",
     "gemm_fp16w", "smoothquant_column_absmax", "smoothquant_factors",
     "smoothquant_quantize_weight", "smoothquant_prepare", "smoothquant_linear",
@@ -48,6 +48,7 @@ STATUS = {
     3: "LI8_ERR_ALIGN",
     4: "LI8_ERR_WORKSPACE",
     5: "LI8_ERR_HIP",
+    6: "LI8_ERR_SCRATCH",
 }
 
 
@@ -89,6 +90,8 @@ def load_library() -> ctypes.CDLL:
     L.llm_int8_plan.argtypes = [i64, i64, i64, vp, vp, vp]
     L.llm_int8_linear.restype = ctypes.c_int
     L.llm_int8_linear.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp, sz, vp]
+    L.llm_int8_linear_noalloc.restype = ctypes.c_int
+    L.llm_int8_linear_noalloc.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp]
     L.llm_int8_prepare.restype = ctypes.c_int
     L.llm_int8_prepare.argtypes = [vp, vp, ctypes.c_float, i64, i64, i64, vp, sz, vp]
     L.llm_int8_gemm.restype = ctypes.c_int
@@ -229,6 +232,32 @@ def linear(X: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, threshold: float
     _check("llm_int8_linear",
            L.llm_int8_linear(_ptr(X), _ptr(Wq), _ptr(sW), float(threshold), T, K, N,
                              _ptr(out), _ptr(ws), ws.numel(), _stream(X.device)))
+    return out
+
+
+# Bytes of the fixed per-GPU array llm_int8_linear_noalloc works in.
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
+
+
+def linear_noalloc(X: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, threshold: float = 6.0,
+                   out: torch.Tensor | None = None):
+    """As ``linear``, with the library's fixed per-GPU scratch array as the
+    workspace (llm_int8_linear_noalloc): the library allocates nothing.
+    Pass ``out`` to allocate nothing here either."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(sW, torch.float32, "sW", 1)
+    T, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or sW.shape[0] != N:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, sW {tuple(sW.shape)}")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    _require(out, torch.float16, "out", 2)
+    _check("llm_int8_linear_noalloc",
+           L.llm_int8_linear_noalloc(_ptr(X), _ptr(Wq), _ptr(sW), float(threshold), T, K, N,
+                                     _ptr(out), _stream(X.device)))
     return out
 
 

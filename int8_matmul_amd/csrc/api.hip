@@ -3,10 +3,18 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "li8_internal.h"
 #include "llm_int8.h"
 
 using namespace li8;
+
+// Workspace of llm_int8_linear_noalloc: one fixed array per GPU, held for
+// the life of the process.  In host code `scratch` is only a handle: its
+// device address, per device, comes from hipGetSymbolAddress and is the
+// only form in which it is passed on.
+static __device__ __align__(256) char scratch[LI8_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -168,6 +176,36 @@ li8_status linear_common(const void *X, const int8_t *Wq, const float *sW, const
                                 static_cast<const char *>(workspace), L, W16 != nullptr, stream));
 }
 
+// Device address of `scratch` on the device that runs `stream`, looked up
+// once per device with that device current.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[kMaxDevices];
+
+li8_status scratch_for(hipStream_t stream, char **out)
+{
+    int cur = 0;
+    hipDevice_t dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &dev) != hipSuccess)
+        return LI8_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return LI8_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess)
+            return LI8_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess)
+            return LI8_ERR_HIP;
+        if (e != hipSuccess || !p)
+            return LI8_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<char *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return LI8_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -181,6 +219,7 @@ const char *li8_status_str(li8_status s)
     case LI8_ERR_ALIGN: return "LI8_ERR_ALIGN";
     case LI8_ERR_WORKSPACE: return "LI8_ERR_WORKSPACE";
     case LI8_ERR_HIP: return "LI8_ERR_HIP";
+    case LI8_ERR_SCRATCH: return "LI8_ERR_SCRATCH";
     }
     return "LI8_UNKNOWN_STATUS";
 }
@@ -308,6 +347,27 @@ li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW, flo
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     return linear_common(X, Wq, sW, nullptr, threshold, T, K, N, Y, workspace, stream);
+}
+
+li8_status llm_int8_linear_noalloc(const void *X, const int8_t *Wq, const float *sW,
+                                   float threshold, int64_t T, int64_t K, int64_t N, void *Y,
+                                   hipStream_t stream)
+{
+    const bool fused = decode_shape(T, K);
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, nullptr, 0, WS_I8, true);
+    if (st == LI8_OK)
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, nullptr, 0, WS_I8, true);
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    char *ws = nullptr;
+    if (!fused) {
+        if (ws_need(T, K, N, WS_I8) > (size_t)LI8_NOALLOC_SCRATCH_BYTES)
+            return LI8_ERR_SCRATCH;
+        st = scratch_for(stream, &ws);
+        if (st != LI8_OK)
+            return st;
+    }
+    return linear_common(X, Wq, sW, nullptr, threshold, T, K, N, Y, ws, stream);
 }
 
 li8_status llm_int8_linear_fp16w(const void *X, const int8_t *Wq, const float *sW, const void *W,

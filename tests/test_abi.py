@@ -16,7 +16,7 @@ import int8_matmul_amd as li8
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "llm_int8.h")
 
-OK, INVALID, SHAPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 4
+OK, INVALID, SHAPE, ALIGN, WORKSPACE, SCRATCH = 0, 1, 2, 3, 4, 6
 # fake, never-dereferenced device addresses
 P = 0x7F0000000000
 P2 = 0x7F0000100000
@@ -40,7 +40,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "li8_status_str", "int8_quantize_weight", "llm_int8_workspace_bytes",
-        "llm_int8_linear_workspace_bytes", "llm_int8_plan",
+        "llm_int8_linear_workspace_bytes", "llm_int8_plan", "llm_int8_linear_noalloc",
         "llm_int8_linear", "llm_int8_prepare", "llm_int8_gemm", "llm_int8_export_stages",
         "llm_int8_linear_fp16w", "llm_int8_prepare_fp16w", "llm_int8_gemm_fp16w",
         "smoothquant_column_absmax", "smoothquant_factors", "smoothquant_quantize_weight",
@@ -155,6 +155,24 @@ def test_linear_validation(lib):
     assert call(N=0, Wq=None, sW=None, Y=None, ws=None, wsb=0) == OK
     assert call(T=0, thr=math.inf) == OK
     assert call(T=0, thr=-0.0) == OK
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free linear: argument checks as for llm_int8_linear,
+    and shapes whose workspace exceeds the fixed array refused before
+    anything is looked up or launched."""
+    f = lib.llm_int8_linear_noalloc
+    assert f(P, P, P, 6.0, 32, 24, 48, P2, None) == SHAPE
+    assert f(None, P, P, 6.0, 32, 64, 48, P2, None) == INVALID
+    assert f(P, P, P, math.nan, 32, 64, 48, P2, None) == INVALID
+    assert f(P, P, MIS, 6.0, 32, 64, 48, P2, None) == ALIGN
+    assert f(P, P, P, 6.0, 32, 64, 48, None, None) == INVALID
+    assert f(None, None, None, 6.0, 0, 64, 48, None, None) == OK   # empty
+    # 70B slice: about 336 MB of workspace against the 128 MiB array
+    assert lib.llm_int8_linear_workspace_bytes(4096, 8192, 28672) > li8.NOALLOC_SCRATCH_BYTES
+    assert f(P, P, P, 6.0, 4096, 8192, 28672, P2, None) == SCRATCH
+    assert lib.llm_int8_linear_workspace_bytes(4096, 4096, 11008) <= li8.NOALLOC_SCRATCH_BYTES
+    assert lib.li8_status_str(SCRATCH).decode() == "LI8_ERR_SCRATCH"
 
 
 def test_prepare_and_gemm_validation(lib):
