@@ -96,9 +96,10 @@ size_t llm_int8_workspace_bytes(int64_t T, int64_t K, int64_t N);
 
 /*
  * Bytes of device workspace that llm_int8_linear itself needs for this
- * shape: 0 when the call takes the one fused few-token kernel (see
- * llm_int8_plan), else the int8 layout (about 3*T*K + N*K bytes, the worst
- * case of every column an outlier).  Returns 0 for an invalid shape too.
+ * shape (see llm_int8_plan): 0 on the fused few-token path; on the split
+ * few-token path about 2*T*K bytes plus 1 KB per slice of K and 16 output
+ * features; else the int8 layout (about 3*T*K + N*K bytes, the worst case
+ * of every column an outlier).  Returns 0 for an invalid shape too.
  */
 size_t llm_int8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N);
 
@@ -112,11 +113,18 @@ size_t llm_int8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N);
  *                                prepared workspace; *tile_m = T,
  *                                *tile_n = 16 output features per row group;
  *            LI8_PATH_TILED      the prepare kernels and the tiled int8 MFMA
- *                                GEMM with output tiles of *tile_m x *tile_n.
+ *                                GEMM with output tiles of *tile_m x *tile_n;
+ *            LI8_PATH_FEW_TOKENS_SPLIT  T <= 16 and K > 8192: K is split
+ *                                across workgroups; llm_int8_linear is a
+ *                                scan of X, the split int8 MFMA product and
+ *                                a finishing kernel (three launches), and
+ *                                llm_int8_gemm the last two on the prepared
+ *                                workspace; *tile_m = T, *tile_n = 16.
  * Returns LI8_ERR_SHAPE for an invalid shape, LI8_ERR_INVALID_ARG for a
  * null pointer.
  */
-enum { LI8_PATH_EMPTY = 0, LI8_PATH_FEW_TOKENS = 1, LI8_PATH_TILED = 2 };
+enum { LI8_PATH_EMPTY = 0, LI8_PATH_FEW_TOKENS = 1, LI8_PATH_TILED = 2,
+       LI8_PATH_FEW_TOKENS_SPLIT = 3 };
 li8_status llm_int8_plan(int64_t T, int64_t K, int64_t N, int32_t *path, int32_t *tile_m,
                          int32_t *tile_n);
 
@@ -131,8 +139,8 @@ li8_status llm_int8_plan(int64_t T, int64_t K, int64_t N, int32_t *path, int32_t
  *   workspace  device buffer of at least llm_int8_linear_workspace_bytes(T,K,N)
  *              bytes, owned by the caller; its contents on entry do not
  *              matter.  Two calls in flight at once need two workspaces.
- *              On the few-token path (llm_int8_plan) none is used, and
- *              NULL is accepted.
+ *              On the fused few-token path (llm_int8_plan) none is used,
+ *              and NULL is accepted.
  * Equivalent to llm_int8_prepare followed by llm_int8_gemm on the same
  * stream and workspace.
  */

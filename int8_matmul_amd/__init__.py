@@ -188,7 +188,7 @@ def linear_workspace_bytes(T: int, K: int, N: int) -> int:
     return int(load_library().llm_int8_linear_workspace_bytes(T, K, N))
 
 
-PATHS = {0: "empty", 1: "few_tokens", 2: "tiled"}
+PATHS = {0: "empty", 1: "few_tokens", 2: "tiled", 3: "few_tokens_split"}
 
 
 def plan(T: int, K: int, N: int) -> dict:
@@ -200,8 +200,8 @@ def plan(T: int, K: int, N: int) -> dict:
 
 
 def few_token_path(T: int, K: int) -> bool:
-    """True if ``linear`` runs as the single fused few-token kernel for T x K."""
-    return plan(T, K, 1)["path"] == "few_tokens"
+    """True if ``linear`` runs on a few-token path (fused or split) for T x K."""
+    return plan(T, K, 1)["path"] in ("few_tokens", "few_tokens_split")
 
 
 def _ws(workspace, T, K, N, device):

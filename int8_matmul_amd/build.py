@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libllm_int8.so")
-SOURCES = ["quant.hip", "gemm.hip", "decode.hip", "smoothquant.hip", "api.hip"]
+SOURCES = ["quant.hip", "gemm.hip", "decode.hip", "decode_split.hip", "smoothquant.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -79,20 +79,44 @@ size_t ws_need(int64_t T, int64_t K, int64_t N, WsKind kind)
     return kind == WS_WIDE ? L.total : L.total_i8;
 }
 
+// Workspace the one-call entry points need: none for the fused few-token
+// kernel, the split layout for few tokens with a long K, else the prepared
+// layout.
+size_t linear_need(int64_t T, int64_t K, int64_t N, WsKind kind)
+{
+    if (decode_shape(T, K))
+        return 0;
+    if (split_shape(T, K))
+        return split_layout(T, K, N).total;
+    return ws_need(T, K, N, kind);
+}
+
 li8_status check_ws(const void *ws, size_t ws_bytes, size_t need)
 {
     if (ws && misaligned(ws))
         return LI8_ERR_ALIGN;
+    if (need == 0)   // (none used: a null workspace is accepted)
+        return LI8_OK;
     if (!ws || ws_bytes < need)
         return LI8_ERR_WORKSPACE;
     return LI8_OK;
 }
 
-// ws_optional: the call takes the one fused few-token kernel, which uses
-// no workspace (a null workspace is then accepted).
+// ONE_CALL: the one-call entry points (llm_int8_linear and its variants),
+// whose workspace need depends on the path (linear_need); the two-call
+// route always needs the prepared layout.
+enum Route { TWO_CALL, ONE_CALL };
+
+li8_status check_route_ws(int64_t T, int64_t K, int64_t N, const void *ws, size_t ws_bytes,
+                          WsKind kind, Route route)
+{
+    return check_ws(ws, ws_bytes, route == ONE_CALL ? linear_need(T, K, N, kind)
+                                                    : ws_need(T, K, N, kind));
+}
+
 li8_status check_linear_args(const void *X, const int8_t *Wq, float threshold, int64_t T,
                              int64_t K, int64_t N, const void *ws, size_t ws_bytes,
-                             WsKind kind, bool ws_optional = false)
+                             WsKind kind, Route route = TWO_CALL)
 {
     li8_status st = check_shape(T, K, N);
     if (st != LI8_OK)
@@ -105,14 +129,12 @@ li8_status check_linear_args(const void *X, const int8_t *Wq, float threshold, i
         return LI8_ERR_INVALID_ARG;
     if (misaligned(X) || misaligned(Wq))
         return LI8_ERR_ALIGN;
-    if (ws_optional)
-        return (ws && misaligned(ws)) ? LI8_ERR_ALIGN : LI8_OK;
-    return check_ws(ws, ws_bytes, ws_need(T, K, N, kind));
+    return check_route_ws(T, K, N, ws, ws_bytes, kind, route);
 }
 
 li8_status check_gemm_args(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
                            const void *Y, const int32_t *acc, const void *ws, size_t ws_bytes,
-                           WsKind kind, bool ws_optional = false)
+                           WsKind kind, Route route = TWO_CALL)
 {
     li8_status st = check_shape(T, K, N);
     if (st != LI8_OK)
@@ -123,9 +145,7 @@ li8_status check_gemm_args(const int8_t *Wq, const float *sW, int64_t T, int64_t
         return LI8_ERR_INVALID_ARG;
     if (misaligned(Wq) || misaligned(sW) || misaligned(Y) || (acc && misaligned(acc)))
         return LI8_ERR_ALIGN;
-    if (ws_optional)
-        return (ws && misaligned(ws)) ? LI8_ERR_ALIGN : LI8_OK;
-    return check_ws(ws, ws_bytes, ws_need(T, K, N, kind));
+    return check_route_ws(T, K, N, ws, ws_bytes, kind, route);
 }
 
 // W16 null: the int8 path; else the fp16-weight variant.  cache: null, or
@@ -138,6 +158,9 @@ li8_status gemm_common(const int8_t *Wq, const float *sW, const uint16_t *W16, i
     if (decode_shape(T, K))
         return from_hip(launch_decode_gemm(Wq, sW, W16, T, K, N, static_cast<uint16_t *>(Y), acc,
                                            static_cast<const char *>(workspace), L, stream));
+    if (split_shape(T, K))
+        return from_hip(launch_split_gemm(Wq, sW, W16, T, K, N, static_cast<uint16_t *>(Y), acc,
+                                          static_cast<const char *>(workspace), L, stream));
     const int8_t *WO =
         cache ? static_cast<const int8_t *>(cache) + cache_layout(K, N).WO : nullptr;
     return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), acc,
@@ -166,6 +189,11 @@ li8_status linear_common(const void *X, const int8_t *Wq, const float *sW, const
         return from_hip(launch_decode_fused(static_cast<const uint16_t *>(X), Wq, sW, W16,
                                             threshold_magnitude(threshold), T, K, N,
                                             static_cast<uint16_t *>(Y), stream));
+    if (split_shape(T, K))
+        return from_hip(launch_split_fused(static_cast<const uint16_t *>(X), Wq, sW, W16,
+                                           threshold_magnitude(threshold), T, K, N,
+                                           static_cast<uint16_t *>(Y), static_cast<char *>(workspace),
+                                           stream));
     const WsLayout L = ws_layout(T, K, N);
     hipError_t e = launch_prepare(static_cast<const uint16_t *>(X), Wq, W16,
                                   threshold_magnitude(threshold), T, K, N,
@@ -244,14 +272,15 @@ size_t llm_int8_workspace_bytes(int64_t T, int64_t K, int64_t N)
 {
     if (check_shape(T, K, N) != LI8_OK)
         return 0;
-    return ws_need(T, K, N, WS_WIDE);
+    const size_t a = ws_need(T, K, N, WS_WIDE), b = linear_need(T, K, N, WS_WIDE);
+    return a > b ? a : b;
 }
 
 size_t llm_int8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N)
 {
-    if (check_shape(T, K, N) != LI8_OK || T == 0 || N == 0 || decode_shape(T, K))
+    if (check_shape(T, K, N) != LI8_OK || T == 0 || N == 0)
         return 0;
-    return ws_need(T, K, N, WS_I8);
+    return linear_need(T, K, N, WS_I8);
 }
 
 li8_status llm_int8_plan(int64_t T, int64_t K, int64_t N, int32_t *path, int32_t *tile_m,
@@ -267,6 +296,10 @@ li8_status llm_int8_plan(int64_t T, int64_t K, int64_t N, int32_t *path, int32_t
         *tile_m = *tile_n = 0;
     } else if (decode_shape(T, K)) {
         *path = LI8_PATH_FEW_TOKENS;
+        *tile_m = (int32_t)T;
+        *tile_n = 16;
+    } else if (split_shape(T, K)) {
+        *path = LI8_PATH_FEW_TOKENS_SPLIT;
         *tile_m = (int32_t)T;
         *tile_n = 16;
     } else {
@@ -338,12 +371,11 @@ li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW, flo
                            int64_t T, int64_t K, int64_t N, void *Y, void *workspace,
                            size_t workspace_bytes, hipStream_t stream)
 {
-    const bool fused = decode_shape(T, K);
     li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes,
-                                      WS_I8, fused);
+                                      WS_I8, ONE_CALL);
     if (st == LI8_OK)
         st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes, WS_I8,
-                             fused);
+                             ONE_CALL);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     return linear_common(X, Wq, sW, nullptr, threshold, T, K, N, Y, workspace, stream);
@@ -353,15 +385,20 @@ li8_status llm_int8_linear_noalloc(const void *X, const int8_t *Wq, const float 
                                    float threshold, int64_t T, int64_t K, int64_t N, void *Y,
                                    hipStream_t stream)
 {
-    const bool fused = decode_shape(T, K);
-    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, nullptr, 0, WS_I8, true);
+    // (the workspace is the scratch array, checked below)
+    li8_status st = check_linear_args(X, Wq, threshold, T, K, N, nullptr, 0, WS_I8, ONE_CALL);
+    if (st == LI8_ERR_WORKSPACE)
+        st = LI8_OK;
     if (st == LI8_OK)
-        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, nullptr, 0, WS_I8, true);
+        st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, nullptr, 0, WS_I8, ONE_CALL);
+    if (st == LI8_ERR_WORKSPACE)
+        st = LI8_OK;
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
     char *ws = nullptr;
-    if (!fused) {
-        if (ws_need(T, K, N, WS_I8) > (size_t)LI8_NOALLOC_SCRATCH_BYTES)
+    const size_t need = linear_need(T, K, N, WS_I8);
+    if (need > 0) {
+        if (need > (size_t)LI8_NOALLOC_SCRATCH_BYTES)
             return LI8_ERR_SCRATCH;
         st = scratch_for(stream, &ws);
         if (st != LI8_OK)
@@ -374,12 +411,11 @@ li8_status llm_int8_linear_fp16w(const void *X, const int8_t *Wq, const float *s
                                  float threshold, int64_t T, int64_t K, int64_t N, void *Y,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    const bool fused = decode_shape(T, K);
     li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes,
-                                      WS_WIDE, fused);
+                                      WS_WIDE, ONE_CALL);
     if (st == LI8_OK)
         st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes, WS_WIDE,
-                             fused);
+                             ONE_CALL);
     if (st == LI8_OK && T > 0 && N > 0 && K > 0) {
         if (!W)
             st = LI8_ERR_INVALID_ARG;
@@ -503,7 +539,7 @@ li8_status llm_int8_prepare_cached(const void *X, const int8_t *Wq, float thresh
         return st;
     // few tokens: the workspace GEMM gathers the outlier weights by index
     // itself; the cache is neither read nor written
-    const bool use = !decode_shape(T, K);
+    const bool use = !decode_shape(T, K) && !split_shape(T, K);
     return from_hip(launch_prepare(static_cast<const uint16_t *>(X), Wq, nullptr,
                                    threshold_magnitude(threshold), T, K, N,
                                    static_cast<char *>(workspace), ws_layout(T, K, N), stream,
@@ -528,17 +564,16 @@ li8_status llm_int8_linear_cached(const void *X, const int8_t *Wq, const float *
                                   void *workspace, size_t workspace_bytes, void *cache,
                                   size_t cache_bytes, hipStream_t stream)
 {
-    const bool fused = decode_shape(T, K);
     li8_status st = check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes,
-                                      WS_I8, fused);
+                                      WS_I8, ONE_CALL);
     if (st == LI8_OK)
         st = check_gemm_args(Wq, sW, T, K, N, Y, nullptr, workspace, workspace_bytes, WS_I8,
-                             fused);
+                             ONE_CALL);
     if (st == LI8_OK && T > 0 && N > 0)
         st = check_cache(cache, cache_bytes, K, N);
     if (st != LI8_OK || T == 0 || N == 0)
         return st;
-    if (decode_shape(T, K))   // one fused kernel; the cache is not used
+    if (decode_shape(T, K) || split_shape(T, K))   // few tokens: the cache is not used
         return linear_common(X, Wq, sW, nullptr, threshold, T, K, N, Y, workspace, stream);
     const WsLayout L = ws_layout(T, K, N);
     hipError_t e = launch_prepare(static_cast<const uint16_t *>(X), Wq, nullptr,

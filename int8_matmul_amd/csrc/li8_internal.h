@@ -121,6 +121,32 @@ hipError_t launch_decode_gemm(const int8_t *Wq, const float *sW, const uint16_t 
                               int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
                               const WsLayout &L, hipStream_t s);
 
+// Few tokens with K past kDecodeMaxK (decode_split.hip): K split into KS
+// slices of KSL columns (a multiple of 512, at most kSplitMaxSlice) over
+// KS x NRGC workgroups, each taking row groups rgc, rgc + NRGC, ...
+constexpr int kSplitMaxSlice = 8192;
+struct SplitPlan {
+    int KS, KSL, NRGC;
+};
+bool split_shape(int64_t T, int64_t K);
+SplitPlan split_plan(int64_t T, int64_t K, int64_t N);
+// Workspace of the one-call route: the prepared stages in the tiled
+// layout's forms (bit set, meta, ascending outlier list, token scales,
+// gathered outlier values of X), the scan's per-strip outlier counts and
+// token maxima, and the partial sums.
+struct SplitLayout {
+    size_t bits, meta, idx, sX, XO, ocnt, pmax, part, total;
+};
+SplitLayout split_layout(int64_t T, int64_t K, int64_t N);
+hipError_t launch_split_fused(const uint16_t *X, const int8_t *Wq, const float *sW,
+                              const uint16_t *W16, uint16_t thr_mag, int64_t T, int64_t K,
+                              int64_t N, uint16_t *Y, char *ws, hipStream_t s);
+// The workspace route: codes, scales and outlier stages from launch_prepare,
+// the partial sums in the WO region (the few-token kernels never read it).
+hipError_t launch_split_gemm(const int8_t *Wq, const float *sW, const uint16_t *W16, int64_t T,
+                             int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
+                             const WsLayout &L, hipStream_t s);
+
 // SmoothQuant-style W8A8 (smoothquant.hip).  Column absmax of fp16 A
 // [rows,K] as fp32; factors s and fl32(1/s); smoothed weight quantization;
 // the per-call token side, which leaves codes, scales and nO = 0 in the

@@ -105,7 +105,8 @@ def test_plan(lib):
     path = ctypes.c_int32()
     assert lib.llm_int8_plan(4, 16, 4, ctypes.byref(path), None, ctypes.byref(path)) == INVALID
     assert li8.few_token_path(16, 8192) and not li8.few_token_path(17, 8192)
-    assert not li8.few_token_path(16, 8208)
+    assert li8.plan(8, 11008, 4096) == dict(path="few_tokens_split", tile_m=8, tile_n=16)
+    assert li8.few_token_path(16, 8208) and li8.plan(16, 8208, 5)["path"] == "few_tokens_split"
 
 
 def test_quantize_weight_validation(lib):

@@ -57,8 +57,8 @@ def draw_shape(rng, i):
     that every output tile shape of the tiled GEMM is drawn; the rest small
     and ragged."""
     kind = i % 4
-    if kind == 0:
-        return int(rng.integers(1, 17)), 16 * int(rng.integers(1, 513)), int(rng.integers(1, 900))
+    if kind == 0:   # up to K = 19200, past the fused few-token kernel's 8192
+        return int(rng.integers(1, 17)), 16 * int(rng.integers(1, 1201)), int(rng.integers(1, 900))
     if kind == 1:
         T, N = int(rng.integers(257, 1101)), int(rng.integers(4000, 17001))
         return T, 16 * int(rng.integers(1, 33)), N
@@ -78,14 +78,15 @@ def draw_case(i):
 
 
 def test_sweep_draws_every_path_and_tile():
-    """The sweep's shapes reach the few-token kernel and each tile shape of
+    """The sweep's shapes reach both few-token paths and each tile shape of
     the tiled GEMM (as the library itself plans them)."""
     seen = set()
     for i in range(CASES):
         T, K, N = draw_shape(np.random.default_rng(1000 + i), i)
         p = li8.plan(T, K, N)
         seen.add((p["path"], p["tile_n"]))
-    assert {("few_tokens", 16), ("tiled", 128), ("tiled", 192), ("tiled", 256)} <= seen, seen
+    assert {("few_tokens", 16), ("few_tokens_split", 16), ("tiled", 128), ("tiled", 192),
+            ("tiled", 256)} <= seen, seen
 
 
 @pytest.mark.parametrize("i", range(CASES))
