@@ -69,6 +69,21 @@ uint16_t threshold_magnitude(float thr)
 
 li8_status from_hip(hipError_t e) { return e == hipSuccess ? LI8_OK : LI8_ERR_HIP; }
 
+// Which outlier counts the prepare kernel may leave ungathered (see
+// launch_prepare): all for the few-token kernels, which gather the weight's
+// outlier columns by index themselves (K); kFoldMin < nO <= fold for the
+// tiled int8 GEMM, which copies them out of its own weight fragments; none
+// for the fp16-weight variant and for calls with an outlier-column cache
+// (the cache must hold what it records).
+GatherSkip gather_above(int64_t T, int64_t K, int64_t N, bool fp16w, bool cached)
+{
+    if (decode_shape(T, K) || split_shape(T, K))
+        return GatherSkip{-1, (int)K};
+    if (fp16w || cached)
+        return GatherSkip{0, 0};
+    return GatherSkip{kFoldMin, gemm_plan(T, K, N).fold};
+}
+
 // Workspace bytes an entry point needs: WIDE for the fp16-weight variant
 // (fp16 outlier weight columns), else the int8 layout.
 enum WsKind { WS_I8, WS_WIDE };
@@ -197,7 +212,8 @@ li8_status linear_common(const void *X, const int8_t *Wq, const float *sW, const
     const WsLayout L = ws_layout(T, K, N);
     hipError_t e = launch_prepare(static_cast<const uint16_t *>(X), Wq, W16,
                                   threshold_magnitude(threshold), T, K, N,
-                                  static_cast<char *>(workspace), L, stream);
+                                  static_cast<char *>(workspace), L, stream, nullptr,
+                                  gather_above(T, K, N, W16 != nullptr, false));
     if (e != hipSuccess)
         return LI8_ERR_HIP;
     return from_hip(launch_gemm(Wq, sW, T, K, N, static_cast<uint16_t *>(Y), nullptr,
@@ -322,7 +338,8 @@ li8_status llm_int8_prepare(const void *X, const int8_t *Wq, float threshold, in
     const WsLayout L = ws_layout(T, K, N);
     return from_hip(launch_prepare(static_cast<const uint16_t *>(X), Wq, nullptr,
                                    threshold_magnitude(threshold), T, K, N,
-                                   static_cast<char *>(workspace), L, stream));
+                                   static_cast<char *>(workspace), L, stream, nullptr,
+                                   gather_above(T, K, N, false, false)));
 }
 
 li8_status llm_int8_prepare_fp16w(const void *X, const void *W, float threshold, int64_t T,
@@ -336,7 +353,8 @@ li8_status llm_int8_prepare_fp16w(const void *X, const void *W, float threshold,
     const WsLayout L = ws_layout(T, K, N);
     return from_hip(launch_prepare(static_cast<const uint16_t *>(X), nullptr,
                                    static_cast<const uint16_t *>(W), threshold_magnitude(threshold),
-                                   T, K, N, static_cast<char *>(workspace), L, stream));
+                                   T, K, N, static_cast<char *>(workspace), L, stream, nullptr,
+                                   gather_above(T, K, N, true, false)));
 }
 
 li8_status llm_int8_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
@@ -543,7 +561,8 @@ li8_status llm_int8_prepare_cached(const void *X, const int8_t *Wq, float thresh
     return from_hip(launch_prepare(static_cast<const uint16_t *>(X), Wq, nullptr,
                                    threshold_magnitude(threshold), T, K, N,
                                    static_cast<char *>(workspace), ws_layout(T, K, N), stream,
-                                   use ? static_cast<char *>(cache) : nullptr));
+                                   use ? static_cast<char *>(cache) : nullptr,
+                                   gather_above(T, K, N, false, use)));
 }
 
 li8_status llm_int8_gemm_cached(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,
@@ -579,7 +598,7 @@ li8_status llm_int8_linear_cached(const void *X, const int8_t *Wq, const float *
     hipError_t e = launch_prepare(static_cast<const uint16_t *>(X), Wq, nullptr,
                                   threshold_magnitude(threshold), T, K, N,
                                   static_cast<char *>(workspace), L, stream,
-                                  static_cast<char *>(cache));
+                                  static_cast<char *>(cache), gather_above(T, K, N, false, true));
     if (e != hipSuccess)
         return LI8_ERR_HIP;
     return gemm_common(Wq, sW, nullptr, T, K, N, Y, nullptr, workspace, stream, cache);

@@ -37,6 +37,7 @@
 //    convert to fp16 into LDS; then each wave writes its sub-tile with
 //    16-byte stores.
 #include <type_traits>
+#include <utility>
 
 #include "li8_internal.h"
 #include "quant_math.h"
@@ -98,12 +99,20 @@ __device__ __forceinline__ void wait_loads_barrier()
 
 constexpr int kOutOfRange = (int)0x80000000;   // buffer offset past any operand
 
+// f(integral_constant<int, I>) for each I of the sequence, in order.
+template <int... I, class F>
+__device__ __forceinline__ void for_each_index(std::integer_sequence<int, I...>, F &&f)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
 template <int BM, int BN, int BKS, int NS, int WM, int WN, int GM, bool F16W, bool STORE_ACC>
 __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     const int8_t *__restrict__ Xq, const int8_t *__restrict__ Wq,
     const float *__restrict__ sX, const float *__restrict__ sW,
     const int32_t *__restrict__ meta, const uint16_t *__restrict__ XO,
-    const int8_t *__restrict__ WO, int T, int K, int N, int tiles_m, int tiles_n,
+    const int8_t *__restrict__ WO, const int32_t *__restrict__ idx_g,
+    const int32_t *__restrict__ wpre_g, int T, int K, int N, int tiles_m, int tiles_n,
     uint16_t *__restrict__ Y, int32_t *__restrict__ acc_out)
 {
     constexpr int NT = WM * WN * 64, NW = WM * WN;
@@ -119,12 +128,25 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     // scales, feature scales and the first 16-column chunk of XO and WO.
     // The staging rows may overlap them; the staging barrier orders that.
     constexpr int WOE = F16W ? 2 : 1;          // bytes per WO element
+    // Fold (int8 path, kFoldMin < nO <= CAP, K <= kFoldMaxK): the tile's
+    // outlier weight columns are copied out of each K stage of the weight
+    // while it sits in LDS, into WOT in the WO chunk layout (rank r of row
+    // n at (r/16)*BN*16 + n*16 + r%16), so the prepare kernel need not
+    // gather them from Wq, a second read of the weight when the outlier
+    // columns are spread over K.  It needs the outlier list and the prefix
+    // counts per bit-set word (stage s starts at word 4s).
+    constexpr int CAP = F16W ? 0 : (BN >= 256 ? 64 : BN >= 192 ? 128 : 256);
+    constexpr int NWMAX = kFoldMaxK / 32;      // bit-set words
     constexpr int PF_SX = NS * SSZ, PF_SW = PF_SX + 4 * BM, PF_XO = PF_SW + 4 * BN;
-    constexpr int PF_WO = PF_XO + 32 * BM, PF_END = PF_WO + 16 * WOE * BN;
+    constexpr int PF_WO = PF_XO + 32 * BM;     // chunk 0 of the gathered WO, or WOT when folding
+    constexpr int WO_B = (16 * WOE * BN > BN * CAP) ? 16 * WOE * BN : BN * CAP;
+    constexpr int PF_IDX = PF_WO + WO_B, PF_WPRE = PF_IDX + 4 * CAP;
+    constexpr int PF_DUMMY = PF_WPRE + (CAP > 0 ? 4 * (NWMAX + 1) : 0);
+    constexpr int PF_END = PF_DUMMY + (CAP > 0 ? NT : 0);
     constexpr int LDSB = (PF_END > STG) ? PF_END : STG;
     static_assert(FM * WM * 32 == BM && FN * WN * 32 == BN, "tile shape");
     static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "loader shape");
-    static_assert(KS % 2 == 0 && NS >= 2, "pipeline shape");
+    static_assert(KS % 2 == 0 && NS >= 2 && BKS == 32 * KS, "pipeline shape");
     __shared__ __attribute__((aligned(1024))) int8_t lds[LDSB];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -150,6 +172,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     asm volatile("" ::"s"(sX), "s"(sW), "s"(XO), "s"(WO), "s"(Y), "s"(acc_out));
     const int nO = min(max(meta[0], 0), K);   // (a bad workspace cannot lengthen the loop)
     asm volatile("" ::"s"(nO));
+    const int nk = (K + BKS - 1) / BKS;
+    const bool fold = CAP > 0 && nO > kFoldMin && nO <= CAP && K <= kFoldMaxK;   // (uniform)
 
     // ---- global -> LDS loaders: load i of this lane fills LDS chunk
     // p = i*NT + wid*64 + lane of the stage (row p / CPR, physical chunk
@@ -233,20 +257,74 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     // One stage.  WAIT: buffer loads allowed in flight at the barrier;
     // ISSUE: request stage kt+NS into the buffer just released; LAST: no
     // next stage.
-    auto stage = [&](int kt, auto wait_c, auto issue_c, auto last_c) {
+    // Fold: copy stage kt's outlier columns (landed, in its ring buffer)
+    // into WOT, right after the barrier that made it visible, when this
+    // wave has no LDS read in flight and the MFMAs of the previous k-step
+    // are still running.  Each thread takes XU (rank, row) items and issues
+    // every LDS access whether or not its item exists (absent items store
+    // to a dummy byte of their own), so the LDS operations in flight stay
+    // countable; a stage with more than XU * NT items copies the rest in a
+    // loop.  (Measured: placed after the MFMAs of a k-step, or spread over
+    // the k-steps, these LDS operations compete with the fragment reads
+    // and cost more.)
+    const int32_t *idx_l = reinterpret_cast<const int32_t *>(lds + PF_IDX);
+    const int32_t *wpre_l = reinterpret_cast<const int32_t *>(lds + PF_WPRE);
+    int8_t *wot = lds + PF_WO;
+    const int nwords = (K + 31) / 32;
+    constexpr int XU = kFoldItems;
+    auto extract = [&](int kt) {
+        const int lo = __builtin_amdgcn_readfirstlane(wpre_l[min(KS * kt, nwords)]);
+        const int hi = __builtin_amdgcn_readfirstlane(wpre_l[min(KS * kt + KS, nwords)]);
+        const int n = (hi - lo) * BN;
+        const int8_t *bst = lds + (kt % NS) * SSZ + ASZ;
+        int rk[XU], row[XU], col[XU];
+#pragma unroll
+        for (int u = 0; u < XU; u++) {
+            const int it = min(u * NT + tid, max(n - 1, 0));
+            const int rr = it / BN;
+            row[u] = it - rr * BN;
+            rk[u] = min(lo + rr, CAP - 1);
+            col[u] = idx_l[rk[u]] - kt * BKS;
+        }
+        int8_t v[XU];
+#pragma unroll
+        for (int u = 0; u < XU; u++) {
+            const int c = min(max(col[u], 0), BKS - 1);
+            v[u] = bst[row[u] * BKS + (((c >> 4) ^ swz<CPR>(row[u])) << 4) + (c & 15)];
+        }
+#pragma unroll
+        for (int u = 0; u < XU; u++) {
+            const bool ok = u * NT + tid < n;
+            int8_t *dst = ok ? wot + (rk[u] >> 4) * (BN * 16) + row[u] * 16 + (rk[u] & 15)
+                             : lds + PF_DUMMY + tid;
+            *dst = v[u];
+        }
+        if (n > XU * NT) {   // (rare: more than XU * NT / BN outlier columns in one stage)
+            for (int it = XU * NT + tid; it < n; it += NT) {
+                const int rr = it / BN, rw = it - rr * BN, r = lo + rr;
+                const int c = idx_l[r] - kt * BKS;
+                wot[(r >> 4) * (BN * 16) + rw * 16 + (r & 15)] =
+                    bst[rw * BKS + (((c >> 4) ^ swz<CPR>(rw)) << 4) + (c & 15)];
+            }
+        }
+    };
+    auto stage = [&](int kt, auto wait_c, auto issue_c, auto last_c, auto fold_c) {
         constexpr int WAIT = decltype(wait_c)::value;
         constexpr bool ISSUE = decltype(issue_c)::value;
         constexpr bool LAST = decltype(last_c)::value;
-#pragma unroll
-        for (int kk = 0; kk < KS; kk++) {
-            const int cur = kk & 1;
+        constexpr bool FOLD = decltype(fold_c)::value;
+        // k-step kk (a compile-time constant: the fold's loop must not stop
+        // the unrolling)
+        auto kstep = [&](auto kk_c) {
+            constexpr int kk = decltype(kk_c)::value;
+            constexpr int cur = kk & 1;
             // Each fragment read of the next k-step is paired with one MFMA
             // of this one, so that the reads do not arrive in a burst that
             // the other wave on the SIMD must wait behind.  (The global ->
             // LDS loads of the last k-step stay grouped: each needs its own
             // M0 value, and the scheduler keeps them together.)
             constexpr int NMF = FM * FN, NRD = FM + FN;
-            if (kk + 1 < KS) {
+            if constexpr (kk + 1 < KS) {
                 __builtin_amdgcn_sched_barrier(0);
                 lread(cur ^ 1, kt, kk + 1);
                 mfmas(cur);
@@ -259,6 +337,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                 __builtin_amdgcn_sched_barrier(0);
             } else if constexpr (!LAST) {
                 wait_loads_barrier<WAIT>();   // stage kt+1 landed; stage kt read by all
+                if constexpr (FOLD) {   // stage kt+1 landed: its outlier columns
+                    extract(kt + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if constexpr (ISSUE)
                     issue(kt + NS);
                 lread(cur ^ 1, kt + 1, 0);
@@ -278,14 +360,14 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                 mfmas(cur);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        }
+        };
+        for_each_index(std::make_integer_sequence<int, KS>{}, kstep);
     };
     using TF = std::false_type;
     using TT = std::true_type;
     using W0 = std::integral_constant<int, 0>;
     using WS = std::integral_constant<int, (LA + LB) * (NS - 2)>;
 
-    const int nk = (K + BKS - 1) / BKS;
     // epilogue prefetch, issued ahead of the first stages: loads complete in
     // order, so once all but the last LA+LB loads of a lane are done, stage
     // 0 and the prefetch have landed while stage 1 may still be in flight;
@@ -314,6 +396,13 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
             prefetch(rXO, PF_XO, B16{}, 2 * BM, [&](int c) {
                 return (int)((unsigned)min(m0 + (c >> 1), T - 1) * 32u + 16u * (c & 1));
             });
+        }
+        if (fold) {   // the outlier list and the word prefix counts (zeros past their ends)
+            const int nw = (K + 31) / 32;
+            prefetch(make_rsrc(idx_g, 4 * K), PF_IDX, B4{}, CAP, [&](int c) { return 4 * c; });
+            prefetch(make_rsrc(wpre_g, 4 * (nw + 1)), PF_WPRE, B4{}, NWMAX + 1, [&](int c) { return 4 * c; });
+        }
+        else if (nO > 0) {   // chunk 0 of the gathered WO
             if constexpr (F16W)
                 prefetch(rWO, PF_WO, B16{}, 2 * BN, [&](int c) {
                     return (int)((unsigned)min(n0 + (c >> 1), N - 1) * 32u + 16u * (c & 1));
@@ -334,13 +423,24 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
         wait_loads_barrier<0>();
         lread(0, 0, 0);
     }
-    int kt = 0;
-    for (; kt + NS < nk; kt++)      // steady state
-        stage(kt, WS{}, TT{}, TF{});
-    for (; kt + 1 < nk; kt++)       // drain
-        stage(kt, W0{}, TF{}, TF{});
-    if (kt < nk)
-        stage(kt, W0{}, TF{}, TT{});
+
+    // the main loop, in a second copy with the fold's copies when this
+    // call folds (the other copy is the plain loop)
+    auto main_loop = [&](auto fold_c) {
+        if constexpr (decltype(fold_c)::value)   // stage 0 landed at the prologue's barrier
+            extract(0);
+        int kt = 0;
+        for (; kt + NS < nk; kt++)      // steady state
+            stage(kt, WS{}, TT{}, TF{}, fold_c);
+        for (; kt + 1 < nk; kt++)       // drain
+            stage(kt, W0{}, TF{}, TF{}, fold_c);
+        if (kt < nk)
+            stage(kt, W0{}, TF{}, TT{}, fold_c);
+    };
+    if (fold)
+        main_loop(TT{});
+    else
+        main_loop(TF{});
 
     // ---- epilogue ----
     // acc[a][b], lane l, register r: token t = tok0 + 32a + (l & 31), feature
@@ -360,7 +460,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                         acc_out[(int64_t)t * N + n] = acc[a][b][r];
                 }
     }
-    if (nk == 0)   // no stage barrier ran: let the prefetched operands land
+    if (nk == 0 || fold)   // prefetched operands landed; fold: every wave's WOT copies done
         wait_loads_barrier<0>();
     // token scales from the prefetch
     const int ltok = wm * FM * 32 + (lane & 31);                 // local token row
@@ -397,6 +497,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
             for (int b = 0; b < FN; b++)
                 ow16[set][b] =
                     __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rWO, voW[b], (int)(cWO * (unsigned)c), 0));
+        } else if (fold) {   // the tile's copy in LDS (ranks past nO: stale codes times XO's zero pad)
+#pragma unroll
+            for (int b = 0; b < FN; b++)
+                ow[set][b] = *reinterpret_cast<const v2u *>(wot + c * (BN * 16) + (lfea + 32 * b) * 16 + khalf * 8);
         } else {
 #pragma unroll
             for (int b = 0; b < FN; b++)
@@ -417,7 +521,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
         }
     };
     if (nch > 0)
-        oload0();
+        oload0();   // (when folding, PF_WO holds WOT, whose chunk 0 has the same layout)
 
     // feature scales, four consecutive per float4
     float4 sw[FN][4];
@@ -563,12 +667,16 @@ hipError_t launch_cfg(const int8_t *Wq, const float *sW, int64_t T, int64_t K, i
     const int32_t *meta = reinterpret_cast<const int32_t *>(ws + L.meta);
     const uint16_t *XO = reinterpret_cast<const uint16_t *>(ws + L.XO);
     const int8_t *WO = WOx ? WOx : reinterpret_cast<const int8_t *>(ws + L.WO);
+    const int32_t *idx = reinterpret_cast<const int32_t *>(ws + L.idx);
+    const int32_t *wpre = reinterpret_cast<const int32_t *>(ws + L.wpre);
     if (acc)
         hipLaunchKernelGGL((k_gemm<BM, BN, BKS, NS, WM, WN, GM, F16W, true>), grid, block, 0, s, Xq, Wq,
-                           sX, sW, meta, XO, WO, (int)T, (int)K, (int)N, tiles_m, tiles_n, Y, acc);
+                           sX, sW, meta, XO, WO, idx, wpre, (int)T, (int)K, (int)N, tiles_m, tiles_n, Y,
+                           acc);
     else
         hipLaunchKernelGGL((k_gemm<BM, BN, BKS, NS, WM, WN, GM, F16W, false>), grid, block, 0, s, Xq, Wq,
-                           sX, sW, meta, XO, WO, (int)T, (int)K, (int)N, tiles_m, tiles_n, Y, acc);
+                           sX, sW, meta, XO, WO, idx, wpre, (int)T, (int)K, (int)N, tiles_m, tiles_n, Y,
+                           acc);
     return hipGetLastError();
 }
 
@@ -589,18 +697,20 @@ constexpr int kCUs = 256;
 
 GemmPlan gemm_plan(int64_t T, int64_t K, int64_t N)
 {
-    (void)K;
     const int64_t tm = (T + 255) / 256;
     const int64_t big = tm * ((N + 255) / 256), mid = tm * ((N + 191) / 192),
                   small = tm * ((N + 127) / 128);
     const double cost_big = (double)((big + kCUs - 1) / kCUs);
     const double cost_mid = 0.75 * 1.15 * (double)((mid + kCUs - 1) / kCUs);
     const double cost_small = 0.5 * 1.35 * (double)((small + kCUs - 1) / kCUs);
+    // the most outlier columns the int8 GEMM copies out of its weight
+    // fragments (its CAP), for K <= kFoldMaxK (its LDS copy of the bit set)
+    const bool fold_k = K <= kFoldMaxK;
     if (cost_small < cost_big && cost_small <= cost_mid)
-        return {256, 128};
+        return {256, 128, fold_k ? 256 : 0};
     if (cost_mid < cost_big)
-        return {256, 192};
-    return {256, 256};
+        return {256, 192, fold_k ? 128 : 0};
+    return {256, 256, fold_k ? 64 : 0};
 }
 
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,

@@ -29,6 +29,8 @@ constexpr int kDecodeMaxBlocks = 256;   // one workgroup per CU
 //   idx  : int32[K]            outlier columns, ascending
 //   sX   : fp32[T]             token scales
 //   Xq   : int8[T,K]           token codes, 0 in outlier columns
+//   wpre : int32[ceil(K/32)+1] outlier columns before bit-set word w
+//                              (column 32 w); wpre[ceil(K/32)] = nO
 //   XO   : fp16, T*K elements  the gathered outlier values in 16-column
 //                              chunks: X[t, idx[i]] at ((i/16)*T + t)*16 + i%16
 //                              for i < nO, zero to the next multiple of 16
@@ -39,7 +41,7 @@ constexpr int kDecodeMaxBlocks = 256;   // one workgroup per CU
 // total_i8 ends the layout after an int8 WO (the int8 and SmoothQuant-style
 // paths); total after an fp16 one (every entry point).
 struct WsLayout {
-    size_t bits, meta, idx, sX, Xq, XO, WO, total_i8, total;
+    size_t bits, meta, idx, wpre, sX, Xq, XO, WO, total_i8, total;
 };
 
 inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
@@ -51,6 +53,7 @@ inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
     L.bits = off; off = align_up(off + 4 * (nwords ? nwords : 1), A);
     L.meta = off; off = align_up(off + 256, A);
     L.idx = off;  off = align_up(off + 4 * (size_t)(K ? K : 1), A);
+    L.wpre = off; off = align_up(off + 4 * (nwords + 1), A);
     L.sX = off;   off = align_up(off + 4 * (size_t)(T ? T : 1), A);
     L.Xq = off;   off = align_up(off + (size_t)T * (size_t)K + 16, A);
     L.XO = off;   off = align_up(off + 2 * (size_t)T * (size_t)K + 16, A);
@@ -89,14 +92,28 @@ hipError_t launch_quantize_weight(const uint16_t *W, int64_t N, int64_t K,
 // instead of those of Wq (the fp16-weight variant).  cache: null, or an
 // outlier-column cache (int8 path only) whose WO receives the gathered
 // columns, the gather being skipped when it already holds this call's set.
+// The weight's outlier columns are left ungathered when skip.lo < nO <=
+// skip.hi: the tiled GEMM's fold range, or every count for the few-token
+// kernels, which gather by index themselves.
+struct GatherSkip {
+    int lo, hi;
+};
 hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W16,
                           uint16_t thr_mag, int64_t T, int64_t K, int64_t N, char *ws,
-                          const WsLayout &L, hipStream_t s, char *cache = nullptr);
+                          const WsLayout &L, hipStream_t s, char *cache = nullptr,
+                          GatherSkip skip = GatherSkip{0, 0});
 hipError_t launch_cache_reset(char *cache, hipStream_t s);
 
-// Tile shape of the tiled GEMM for a call of this shape (gemm.hip).
+// Tile shape of the tiled GEMM for a call of this shape (gemm.hip), and
+// fold: the most outlier columns whose weight columns its int8 variant
+// copies out of the weight fragments it multiplies (0: none).  A call with
+// kFoldMin < nO <= fold needs no gathered WO; with fewer the gather is
+// cheap (few columns), and the plain main loop is kept.
+constexpr int kFoldMin = 16;
+constexpr int64_t kFoldMaxK = 8192;
+constexpr int kFoldItems = 4;   // (rank, row) items per thread and K stage copied without a loop
 struct GemmPlan {
-    int bm, bn;
+    int bm, bn, fold;
 };
 GemmPlan gemm_plan(int64_t T, int64_t K, int64_t N);
 

@@ -220,8 +220,10 @@ template <int ROWS, bool REG, int RREG>
 __global__ __launch_bounds__(kThreads) void k_prepare(
     const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq,
     const uint16_t *__restrict__ W16, int T, int K, int N,
-    int wrows, const uint32_t *__restrict__ bits_g, int32_t *__restrict__ meta,
-    int32_t *__restrict__ idx_g, float *__restrict__ sX, int8_t *__restrict__ Xq,
+    int wrows, int fold_lo, int fold_hi, const uint32_t *__restrict__ bits_g,
+    int32_t *__restrict__ meta, int32_t *__restrict__ idx_g, int32_t *__restrict__ wpre,
+    float *__restrict__ sX,
+    int8_t *__restrict__ Xq,
     uint16_t *__restrict__ XO, int8_t *__restrict__ WO, int32_t *__restrict__ cache_hdr,
     uint32_t *__restrict__ cache_bits)
 {
@@ -374,6 +376,9 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
         }
         if (tid == 0)
             meta[0] = nO;
+        // outlier columns before each bit-set word (the tiled GEMM's fold)
+        for (int w = tid; w <= nw; w += kThreads)
+            wpre[w] = w < nw ? pre[w] : nO;
     }
     // Outlier-column cache (cache_hdr non-null): WO is the cache's copy of
     // the gathered columns.  If the cache holds this call's exact set, the
@@ -393,7 +398,9 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
         __syncthreads();
         miss = miss_s != 0;
     }
-    if (!miss || nO == 0)   // nothing to gather
+    // (the tiled GEMM copies the weight's outlier columns itself when
+    // fold_lo < nO <= fold_hi)
+    if (!miss || nO == 0 || (nO > fold_lo && nO <= fold_hi))   // nothing to gather, or the GEMM takes them
         return;
     // list the non-zero words once (one wave, ballot compaction), then
     // visit (row, non-zero word) pairs only
@@ -534,7 +541,7 @@ hipError_t launch_cache_reset(char *cache, hipStream_t s)
 
 hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W16,
                           uint16_t thr_mag, int64_t T, int64_t K, int64_t N, char *ws,
-                          const WsLayout &L, hipStream_t s, char *cache)
+                          const WsLayout &L, hipStream_t s, char *cache, GatherSkip skip)
 {
     const CacheLayout C = cache_layout(K, N);
     uint32_t *bits = reinterpret_cast<uint32_t *>(ws + L.bits);
@@ -570,8 +577,9 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
                   : (narrow ? k_prepare<kPrepRows, false, 2> : k_prepare<kPrepRows, false, 4>);
     auto launch = [&](auto KP) {
     hipLaunchKernelGGL(KP, dim3((unsigned)(xblocks + wblocks)), dim3(kThreads), lds, s, X, Wq,
-                       W16, (int)T, (int)K, (int)N, wrows, bits, meta,
-                       reinterpret_cast<int32_t *>(ws + L.idx),
+                       W16, (int)T, (int)K, (int)N, wrows, skip.lo, skip.hi, bits,
+                       meta, reinterpret_cast<int32_t *>(ws + L.idx),
+                       reinterpret_cast<int32_t *>(ws + L.wpre),
                        reinterpret_cast<float *>(ws + L.sX),
                        reinterpret_cast<int8_t *>(ws + L.Xq),
                        reinterpret_cast<uint16_t *>(ws + L.XO),

@@ -138,15 +138,18 @@ def test_few_tokens_leave_the_cache_alone():
 def test_reset_after_the_weight_changes_and_a_hit_reuses_the_columns():
     """A hit reads the cached columns instead of gathering: shown by handing
     the cache a different weight without a reset (outside the contract), which
-    must give a different Y; after llm_int8_cache_reset the result is right."""
+    must give a different Y; after llm_int8_cache_reset the result is right.
+    (Token-sparse outliers give more outlier columns than the GEMM copies out
+    of its own K stages, at most 256, so the GEMM reads the cache's columns.)"""
     T, K, N = 256, 1024, 512
-    W1, xs = batches(T, K, N, seed=3)
+    W1, xs = batches(T, K, N, sparse=2e-3, seed=3)
     W2 = (W1.astype(np.float32) * -1.5).astype(np.float16)
     X = dev(xs["a"])
     Wq1, sW1 = li8.quantize_weight(dev(W1))
     Wq2, sW2 = li8.quantize_weight(dev(W2))
     cache = li8.new_cache(K, N, DEV)
     li8.linear_cached(X, Wq1, sW1, cache)
+    assert li8.cache_stats(cache)["nO"] > 256
     stale = li8.linear_cached(X, Wq2, sW2, cache)
     assert li8.cache_stats(cache)["hits"] == 1
     assert not same_bits(stale, li8.linear(X, Wq2, sW2))

@@ -209,6 +209,33 @@ def test_outlier_count_at_gather_capacity(n_out):
     assert o["nO"] == n_out
 
 
+@pytest.mark.parametrize("T,N,tile_n,cap", [(1000, 16300, 256, 64), (1000, 8320, 192, 128),
+                                             (300, 520, 128, 256)])
+@pytest.mark.parametrize("which", ["min", "min+1", "cap", "cap+1", "dense stage"])
+def test_gemm_fold_capacity(T, N, tile_n, cap, which):
+    """With more than 16 and at most cap outlier columns (64, 128, 256 by
+    tile width) the tiled GEMM copies their weight columns out of the K
+    stages it streams through LDS; otherwise the prepare kernel gathers
+    them.  Both sides of each limit, the columns spread over K, one in the
+    ragged last stage; and 40 columns in one 128-column stage, more than a
+    stage's fixed share of copies (2048 / tile width)."""
+    K = 1040
+    n_out = {"min": 16, "min+1": 17, "cap": cap, "cap+1": cap + 1, "dense stage": 40}[which]
+    assert li8.plan(T, K, N) == dict(path="tiled", tile_m=256, tile_n=tile_n)
+    rng = np.random.default_rng(9000 + cap + n_out)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    if which == "dense stage":
+        cols = np.sort(rng.choice(128, n_out - 1, replace=False) + 256)
+    else:
+        cols = np.sort(rng.choice(K - 16, n_out - 1, replace=False))
+    cols = np.append(cols, K - 5)
+    X[:, cols] = rng.choice([-1.0, 1.0], (T, n_out)) * rng.uniform(20, 60, (T, n_out))
+    X = X.astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = check_full(X, W, 6.0, f"fold capacity {tile_n}: {n_out} outlier columns")
+    assert o["nO"] == n_out
+
+
 @pytest.mark.parametrize("n_out", [32, 33, 256, 257, 513])
 def test_few_token_outlier_list_capacity(n_out):
     """The few-token kernel lists up to 256 outlier columns in LDS and
