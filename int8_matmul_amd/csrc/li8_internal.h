@@ -22,9 +22,16 @@ constexpr int kDecodeMaxT = 16;
 constexpr int kDecodeMaxK = 8192;
 constexpr int kDecodeMaxBlocks = 256;   // one workgroup per CU
 
+// Row strips of the outlier detection: each writes its own partial bit
+// set, and the quantization kernel ORs the strips' words.
+constexpr int kDetectParts = 16;
+
 // Device workspace carved into fixed regions.  Offsets depend only on the
 // shape (T, K, N), never on the data, so the host needs no readback.
-//   bits : uint32[ceil(K/32)]  outlier column bit set (cleared every call)
+//   part : uint32[kDetectParts][ceil(K/32)]  per-row-strip partial bit sets
+//                              (every word of the strips in use written by
+//                              the detection kernel, none read before)
+//   bits : uint32[ceil(K/32)]  outlier column bit set (the strips' OR)
 //   meta : int32[64]           meta[0] = nO
 //   idx  : int32[K]            outlier columns, ascending
 //   sX   : fp32[T]             token scales
@@ -41,7 +48,7 @@ constexpr int kDecodeMaxBlocks = 256;   // one workgroup per CU
 // total_i8 ends the layout after an int8 WO (the int8 and SmoothQuant-style
 // paths); total after an fp16 one (every entry point).
 struct WsLayout {
-    size_t bits, meta, idx, wpre, sX, Xq, XO, WO, total_i8, total;
+    size_t part, bits, meta, idx, wpre, sX, Xq, XO, WO, total_i8, total;
 };
 
 inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
@@ -50,6 +57,7 @@ inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N)
     WsLayout L;
     size_t off = 0;
     size_t nwords = (size_t)((K + 31) / 32);
+    L.part = off; off = align_up(off + 4 * kDetectParts * (nwords ? nwords : 1), A);
     L.bits = off; off = align_up(off + 4 * (nwords ? nwords : 1), A);
     L.meta = off; off = align_up(off + 256, A);
     L.idx = off;  off = align_up(off + 4 * (size_t)(K ? K : 1), A);

@@ -87,73 +87,78 @@ __global__ __launch_bounds__(kThreads) void k_quantize_weight(
 }
 
 // ---------------------------------------------------------------------------
-// Clear the outlier bit set and the meta words (a kernel rather than a
-// memset so that the sequence stays capturable in a HIP graph).
-// ---------------------------------------------------------------------------
-__global__ void k_clear(uint32_t *__restrict__ bits, int nwords, int32_t *__restrict__ meta)
-{
-    int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < nwords)
-        bits[i] = 0u;
-    if (i < 64)
-        meta[i] = 0;
-}
-
-// ---------------------------------------------------------------------------
-// Outlier detection.  Block (x, y) covers 2048 columns (8 per thread) of
-// rows [y*R, y*R+R).  Rows are read in batches of kDetectRows with every load of a
-// batch issued before any is used (these short streaming kernels are
-// latency-bound otherwise); rows past the end re-read the last row, which
-// leaves the maximum unchanged.  The per-column magnitude max is kept
-// packed in registers; one compare per column at the end; four lanes
-// combine their 8-bit masks into one 32-bit word, and non-zero words are
-// OR-ed into the bit set.
+// Outlier detection.  Block (x, y) covers CPB 8-column chunks (CPB/4
+// bit-set words) of the row strip [y*R, y*R+R): thread (rl, cl) reads
+// chunk x*CPB + cl of rows t0+rl, t0+rl+RL, ... (RL = 256/CPB row lanes),
+// in batches of kDetectRows loads issued before any is used (these short
+// streaming kernels are latency-bound otherwise); rows past the strip
+// re-read its last row, which leaves the maximum unchanged.  The per-column
+// magnitude max is kept packed in registers, one compare per column at the
+// end, and the row lanes' flags are OR-ed through LDS.  Each block stores
+// its words of strip y's partial bit set with plain stores: every word of
+// every strip is written by exactly one block, so nothing is cleared
+// first and no atomics are needed; k_prepare ORs the strips.
 // ---------------------------------------------------------------------------
 typedef li8_us2 us2;
 
 constexpr int kDetectRows = 16;   // rows per load batch
 
+template <int CPB>
 __global__ __launch_bounds__(kThreads) void k_detect(
     const uint16_t *__restrict__ X, int T, int K, int R, uint32_t thr_mag,
-    uint32_t *__restrict__ bits)
+    uint32_t *__restrict__ part)
 {
-    const int nchunk = K / 8;
-    const int c = blockIdx.x * kThreads + threadIdx.x;
+    static_assert(CPB % 4 == 0 && CPB <= kThreads && kThreads % CPB == 0, "chunks per block");
+    constexpr int RL = kThreads / CPB;
+    __shared__ uint32_t fl[RL][CPB];
+    const int nchunk = K / 8, nw = (K + 31) / 32;
+    const int cl = threadIdx.x % CPB, rl = threadIdx.x / CPB;
+    const int c = blockIdx.x * CPB + cl;
     const int t0 = blockIdx.y * R;
     const int t1 = min(T, t0 + R);
     us2 mx[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
     if (c < nchunk) {
         const uint4 *p = reinterpret_cast<const uint4 *>(X) + c;
         const int64_t stride = K / 8;
-        for (int tb = t0; tb < t1; tb += kDetectRows) {
+        for (int tb = t0 + rl; tb < t1; tb += RL * kDetectRows) {
             uint4 v[kDetectRows];
 #pragma unroll
             for (int u = 0; u < kDetectRows; u++)
-                v[u] = p[(int64_t)min(tb + u, t1 - 1) * stride];
+                v[u] = p[(int64_t)min(tb + u * RL, t1 - 1) * stride];
 #pragma unroll
             for (int u = 0; u < kDetectRows; u++)
                 column_max8(mx, v[u]);
         }
     }
-    const uint32_t m8 = outlier_flags8(mx, thr_mag);
-    // chunk c holds columns 8c..8c+7 = bits 8*(c%4).. of word c/4
-    uint32_t word = m8 << (8 * (c & 3));
-    word |= (uint32_t)__shfl_xor((int)word, 1, 64);
-    word |= (uint32_t)__shfl_xor((int)word, 2, 64);
-    if ((c & 3) == 0 && c < nchunk && word != 0u)
-        atomicOr(bits + (c >> 2), word);
+    fl[rl][cl] = outlier_flags8(mx, thr_mag);
+    __syncthreads();
+    if ((int)threadIdx.x < CPB) {
+        uint32_t f = 0;
+#pragma unroll
+        for (int r = 0; r < RL; r++)
+            f |= fl[r][threadIdx.x];
+        // chunk c holds columns 8c..8c+7 = bits 8*(c%4).. of word c/4; the
+        // four chunks of a word sit in four consecutive lanes
+        uint32_t word = f << (8 * (threadIdx.x & 3));
+        word |= (uint32_t)__shfl_xor((int)word, 1, 64);
+        word |= (uint32_t)__shfl_xor((int)word, 2, 64);
+        const int w = (blockIdx.x * CPB + threadIdx.x) >> 2;
+        if ((threadIdx.x & 3) == 0 && w < nw)
+            part[(int64_t)blockIdx.y * nw + w] = word;
+    }
 }
 
 // Bit-set words held in registers per thread by k_prepare (nw <= 256,
 // i.e. K <= 8192); longer bit sets are read from global memory.
 constexpr int kBitsPerThread = 1;
 
-// Load the bit set into LDS and write the exclusive prefix of the
-// popcounts per word; returns nO (the total) to every thread.  Thread tid
-// owns words [tid*per, tid*per + per); with REG, bw already holds them
-// (nw <= kBitsPerThread * kThreads).
+// Load the bit set into LDS (the OR of the nparts row strips' partial
+// sets) and write the exclusive prefix of the popcounts per word; returns
+// nO (the total) to every thread.  Thread tid owns words [tid*per,
+// tid*per + per); with REG, bw already holds them (nw <= kBitsPerThread *
+// kThreads).
 template <bool REG>
-__device__ int load_bits_and_scan(const uint32_t *__restrict__ bits_g, int nw,
+__device__ int load_bits_and_scan(const uint32_t *__restrict__ parts, int nparts, int nw,
                                   uint32_t *bits, int32_t *pre, int32_t *scan,
                                   const uint32_t (&bw)[kBitsPerThread])
 {
@@ -173,7 +178,9 @@ __device__ int load_bits_and_scan(const uint32_t *__restrict__ bits_g, int nw,
         }
     } else {
         for (int w = w0; w < w1; w++) {
-            uint32_t b = bits_g[w];
+            uint32_t b = 0u;
+            for (int y = 0; y < nparts; y++)
+                b |= parts[(int64_t)y * nw + w];
             bits[w] = b;
             s += __popc(b);
         }
@@ -220,8 +227,8 @@ template <int ROWS, bool REG, int RREG>
 __global__ __launch_bounds__(kThreads) void k_prepare(
     const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq,
     const uint16_t *__restrict__ W16, int T, int K, int N,
-    int wrows, int fold_lo, int fold_hi, const uint32_t *__restrict__ bits_g,
-    int32_t *__restrict__ meta, int32_t *__restrict__ idx_g, int32_t *__restrict__ wpre,
+    int wrows, int fold_lo, int fold_hi, const uint32_t *__restrict__ parts, int nparts,
+    uint32_t *__restrict__ bits_g, int32_t *__restrict__ meta, int32_t *__restrict__ idx_g, int32_t *__restrict__ wpre,
     float *__restrict__ sX,
     int8_t *__restrict__ Xq,
     uint16_t *__restrict__ XO, int8_t *__restrict__ WO, int32_t *__restrict__ cache_hdr,
@@ -240,19 +247,28 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
     const bool xblock = (int)blockIdx.x < xblocks;
     const int t0 = blockIdx.x * ROWS;
 
-    // Loads first, all unconditional: this thread's bit-set words, then the
-    // token rows (buffer loads; chunks past the row and the lanes of
-    // weight-gather blocks use offset 2^31, past the buffer whenever X is
-    // under 2 GiB, else a valid address whose value is not used).  Loads behind branches would make the compiler wait for all
-    // of them at the first use; this way the bit-set scan waits only for
-    // the bit-set words (loads complete in order) while the rows arrive.
+    // Loads first, all unconditional: this thread's bit-set words in every
+    // row strip's partial set, then the token rows (buffer loads; chunks
+    // past the row and the lanes of weight-gather blocks use offset 2^31,
+    // past the buffer whenever X is under 2 GiB, else a valid address whose
+    // value is not used).  Loads behind branches would make the compiler
+    // wait for all of them at the first use; this way the bit-set scan
+    // waits only for the bit-set words (loads complete in order) while the
+    // rows arrive.  Strips past nparts re-read the last one (an OR of the
+    // same word twice), so their count is no branch either.
     uint32_t bw[kBitsPerThread] = {};
     if constexpr (REG) {
         const int per = (nw + kThreads - 1) / kThreads;
         const int w0 = tid * per, wl = nw > 0 ? nw - 1 : 0;   // (the region has >= 1 word)
 #pragma unroll
-        for (int i = 0; i < kBitsPerThread; i++)
-            bw[i] = bits_g[min(w0 + i, wl)];
+        for (int i = 0; i < kBitsPerThread; i++) {
+            const int w = min(w0 + i, wl);
+            uint32_t b = 0u;
+#pragma unroll
+            for (int y = 0; y < kDetectParts; y++)
+                b |= parts[min(y, nparts - 1) * nw + w];
+            bw[i] = b;
+        }
     }
     __builtin_amdgcn_sched_barrier(0);   // (keep the row loads after them)
     uint4 v[ROWS][RREG];
@@ -272,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
             }
         }
     }
-    const int nO = load_bits_and_scan<REG>(bits_g, nw, bits, pre, scan, bw);
+    const int nO = load_bits_and_scan<REG>(parts, nparts, nw, bits, pre, scan, bw);
     const int nO16 = (nO + 15) & ~15;   // <= K since K % 16 == 0
 
     if (xblock) {
@@ -376,9 +392,13 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
         }
         if (tid == 0)
             meta[0] = nO;
-        // outlier columns before each bit-set word (the tiled GEMM's fold)
-        for (int w = tid; w <= nw; w += kThreads)
+        // outlier columns before each bit-set word (the tiled GEMM's fold),
+        // and the merged bit set (for the cache's record and the stage export)
+        for (int w = tid; w <= nw; w += kThreads) {
             wpre[w] = w < nw ? pre[w] : nO;
+            if (w < nw)
+                bits_g[w] = bits[w];
+        }
     }
     // Outlier-column cache (cache_hdr non-null): WO is the cache's copy of
     // the gathered columns.  If the cache holds this call's exact set, the
@@ -522,6 +542,38 @@ __global__ void k_cache_reset(int32_t *__restrict__ hdr)
         hdr[threadIdx.x] = 0;
 }
 
+// The detection grid: CPB chunks per block (of 16..256) and gy <= 16 row
+// strips.  The first (rows per thread, CPB) pair, in that order of
+// preference, that gives at least 256 workgroups with at most that many
+// rows per thread (two load batches, then one, then half of one); else the
+// most workgroups the shape allows.  (Two batches per workgroup measured
+// fastest at 4096 x 4096 and 4096 x 8192.)
+struct DetectGrid {
+    int cpb, gx, gy, R;
+};
+
+DetectGrid detect_grid(int64_t T, int64_t K)
+{
+    const int64_t nchunk = K / 8;
+    if (nchunk == 0 || T == 0)
+        return {16, 0, 0, 0};
+    auto make = [&](int cpb, int64_t rpt) {
+        const int64_t rl = kThreads / cpb;
+        const int64_t gy = std::min<int64_t>(kDetectParts, (T + rl * rpt - 1) / (rl * rpt));
+        const int64_t R = (T + gy - 1) / gy;
+        return DetectGrid{cpb, (int)((nchunk + cpb - 1) / cpb), (int)gy, (int)R};
+    };
+    for (int64_t rpt : {2 * kDetectRows, kDetectRows, kDetectRows / 2}) {
+        for (int cpb : {256, 128, 64, 32, 16}) {
+            const DetectGrid g = make(cpb, rpt);
+            const int64_t rows = ((int64_t)g.R + kThreads / cpb - 1) / (kThreads / cpb);
+            if ((int64_t)g.gx * g.gy >= 256 && rows <= rpt)
+                return g;
+        }
+    }
+    return make(16, kDetectRows / 2);
+}
+
 } // namespace
 
 hipError_t launch_quantize_weight(const uint16_t *W, int64_t N, int64_t K, int8_t *Wq,
@@ -545,28 +597,22 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
 {
     const CacheLayout C = cache_layout(K, N);
     uint32_t *bits = reinterpret_cast<uint32_t *>(ws + L.bits);
+    uint32_t *part = reinterpret_cast<uint32_t *>(ws + L.part);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + L.meta);
     const int nw = (int)((K + 31) / 32);
-    hipLaunchKernelGGL(k_clear, dim3((unsigned)((max(nw, 64) + 255) / 256)), dim3(256), 0, s,
-                       bits, nw, meta);
-    const int nchunk = (int)(K / 8);
-    if (nchunk > 0) {
-        const int gx = (nchunk + kThreads - 1) / kThreads;
-        // rows per block: a multiple of the load batch.  Two batches per
-        // block when that still gives at least 256 workgroups (measured
-        // fastest at 4096 x 4096 and 4096 x 8192), else about 256
-        // workgroups of one batch; grid.y <= 65535
-        const int64_t gy2 = (T + 2 * kDetectRows - 1) / (2 * kDetectRows);
-        int gy = gx * gy2 >= 256
-                     ? (int)std::min<int64_t>(gy2, 65535)
-                     : (int)std::min<int64_t>((T + kDetectRows - 1) / kDetectRows, std::max(1, 256 / gx));
-        int R = (int)((T + gy - 1) / gy);
-        R = (R + kDetectRows - 1) / kDetectRows * kDetectRows;
-        while ((T + R - 1) / R > 65535)
-            R *= 2;
-        gy = (int)((T + R - 1) / R);
-        hipLaunchKernelGGL(k_detect, dim3(gx, gy), dim3(kThreads), 0, s, X, (int)T, (int)K,
-                           R, (uint32_t)thr_mag, bits);
+    const DetectGrid dg = detect_grid(T, K);
+    if (dg.gy > 0) {
+        auto launch_detect = [&](auto KD) {
+            hipLaunchKernelGGL(KD, dim3((unsigned)dg.gx, (unsigned)dg.gy), dim3(kThreads), 0, s, X,
+                               (int)T, (int)K, dg.R, (uint32_t)thr_mag, part);
+        };
+        switch (dg.cpb) {
+        case 256: launch_detect(k_detect<256>); break;
+        case 128: launch_detect(k_detect<128>); break;
+        case 64: launch_detect(k_detect<64>); break;
+        case 32: launch_detect(k_detect<32>); break;
+        default: launch_detect(k_detect<16>); break;
+        }
     }
     const int wrows = 32;
     const int64_t wblocks = (N + wrows - 1) / wrows;
@@ -577,8 +623,8 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
                   : (narrow ? k_prepare<kPrepRows, false, 2> : k_prepare<kPrepRows, false, 4>);
     auto launch = [&](auto KP) {
     hipLaunchKernelGGL(KP, dim3((unsigned)(xblocks + wblocks)), dim3(kThreads), lds, s, X, Wq,
-                       W16, (int)T, (int)K, (int)N, wrows, skip.lo, skip.hi, bits,
-                       meta, reinterpret_cast<int32_t *>(ws + L.idx),
+                       W16, (int)T, (int)K, (int)N, wrows, skip.lo, skip.hi, part,
+                       std::max(dg.gy, 1), bits, meta, reinterpret_cast<int32_t *>(ws + L.idx),
                        reinterpret_cast<int32_t *>(ws + L.wpre),
                        reinterpret_cast<float *>(ws + L.sX),
                        reinterpret_cast<int8_t *>(ws + L.Xq),

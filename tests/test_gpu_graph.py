@@ -1,8 +1,8 @@
 """Calls captured in a HIP graph and replayed, and calls on two streams.
 
-The calls allocate nothing given a workspace, never synchronize and clear
-their device state with kernels of their own (no memset nodes), so a
-captured call must give the eager call's output on every replay.  Each case
+The calls allocate nothing given a workspace, never synchronize and read
+no device state they have not written in the same call (no memset nodes),
+so a captured call must give the eager call's output on every replay.  Each case
 captures one call, replays it several times with eager work on the same
 buffers in between (other inputs through the same workspace), and checks
 every replay bit for bit against the eager output.  Shapes cover the tiled

@@ -221,7 +221,8 @@ def test_gemm_fold_capacity(T, N, tile_n, cap, which):
     stage's fixed share of copies (2048 / tile width)."""
     K = 1040
     n_out = {"min": 16, "min+1": 17, "cap": cap, "cap+1": cap + 1, "dense stage": 40}[which]
-    assert li8.plan(T, K, N) == dict(path="tiled", tile_m=256, tile_n=tile_n)
+    assert li8.plan(T, K, N) == dict(path="tiled", tile_m=256, tile_n=tile_n,
+                                     fold_lo=16, fold_hi=cap)
     rng = np.random.default_rng(9000 + cap + n_out)
     X = rng.standard_normal((T, K)).astype(np.float32)
     if which == "dense stage":
@@ -336,6 +337,41 @@ def test_determinism_and_canary():
     assert np.all(host(buf[T * N:]) == sentinel)
 
 
+@pytest.mark.parametrize("T,K,N", [
+    (300, 1040, 520),     # tiled path, few detection strips
+    (4096, 512, 300),     # tiled path, all 16 detection strips
+    (8, 4096, 300),       # few tokens (prepare + gemm route)
+    (8, 11008, 300),      # few tokens, split K (prepare + gemm route)
+])
+def test_dirty_workspace(T, K, N):
+    """A workspace's contents on entry do not matter: every byte set (a
+    partial bit set read before it was written would flag every column)
+    gives the same stages and output as a zeroed one, for linear and for
+    prepare + gemm."""
+    X, W, _ = workloads.make("prefill_7b_ffn_up", T=T, K=K, N=N)
+    Xd, Wd = dev(X), dev(W)
+    Wq, sW = li8.quantize_weight(Wd)
+    out = {}
+    for fill in (0, 255):
+        ws = li8.new_workspace(T, K, N, DEV)
+        ws.fill_(fill)
+        Y = li8.linear(Xd, Wq, sW, 6.0, workspace=ws)
+        ws.fill_(fill)
+        li8.prepare(Xd, Wq, 6.0, ws)
+        st = {k: host(v).copy() for k, v in li8.export_stages(ws, T, K, N).items()}
+        Y2 = li8.gemm(Wq, sW, T, ws)
+        out[fill] = (host(Y).copy(), host(Y2).copy(), st)
+    say(f"case dirty workspace {T}x{K}x{N}: {int(out[0][2]['n_outliers'][0])} outlier columns")
+    for a, b in zip(out[0][:2], out[255][:2]):
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    nO = int(out[0][2]["n_outliers"][0])
+    assert int(out[255][2]["n_outliers"][0]) == nO
+    for k in ("outlier_bits", "sX", "Xq"):
+        assert np.array_equal(out[0][2][k], out[255][2][k]), k
+    assert np.array_equal(out[0][2]["outlier_idx"][:nO], out[255][2]["outlier_idx"][:nO])
+    assert np.array_equal(out[0][0].view(np.uint16), out[0][1].view(np.uint16))
+
+
 @pytest.mark.parametrize("T,K,N,tile_n", [
     (1000, 272, 16300, 256),   # 4 x 64 tiles of 256x256: exactly one round
     (1000, 272, 8320, 192),    # 4 x 44 tiles of 256x192, the last 64 features wide
@@ -345,7 +381,8 @@ def test_tile_shapes_ragged(T, K, N, tile_n):
     """Each output tile shape of the tiled GEMM on ragged T and N, every
     element against the oracle (int8 path), and the fp16-weight variant's
     output and accumulators on the same tiles."""
-    assert li8.plan(T, K, N) == dict(path="tiled", tile_m=256, tile_n=tile_n)
+    p = li8.plan(T, K, N)
+    assert (p["path"], p["tile_m"], p["tile_n"]) == ("tiled", 256, tile_n)
     w = workloads.WORKLOADS["prefill_7b_ffn_up"]
     X, _ = workloads.make_activation(w, seed=5 + tile_n, T=T, K=K)
     W = workloads.make_weight(w, seed=6 + tile_n, N=N, K=K)
