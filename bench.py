@@ -11,7 +11,12 @@ before timing, as it is at load time.  Inputs are seeded synthetic tensors
 
 The K timed steps are K calls of llm_int8_linear captured in one HIP graph
 (checked against an eager call), replayed between two synchronizations:
-host launch cost does not pace the short few-token calls.
+host launch cost does not pace the short few-token calls.  Untimed replays
+of the same graph come first, for --settle-ms of GPU time, so that the
+timed ones run at the steady-state shader clock.  Two cache states are
+measured: warm (one buffer set, reused by every call) and cold (rotating
+copies of every buffer, more than twice the 256 MB Infinity Cache per
+cycle); `value` is the warm one unless --cold.
 
 Prints one JSON line.  `value` is the effective throughput 2*T*N*K / time
 of a step, in TOPS.  `roofline` is for the dominant kernel: the tiled GEMM
@@ -23,6 +28,7 @@ sample of the same call.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -52,8 +58,15 @@ def parse():
                          "llm_int8_linear_cached with an outlier-column cache (every call "
                          "after the first reuses the gathered weight columns)")
     ap.add_argument("--cold", action="store_true",
-                    help="rotate copies of the call's buffers (more than 2 x 256 MB per cycle) "
-                         "so that no call finds its operands in the Infinity Cache")
+                    help="make `value` the cold-cache measurement (copies of the call's buffers "
+                         "rotated, more than 2 x 256 MB per cycle, so that no call finds its "
+                         "operands in the Infinity Cache); both are measured either way")
+    ap.add_argument("--shape", default=None, metavar="T,K,N",
+                    help="the named workload's input recipe at another shape (for counter "
+                         "attribution runs; the line then names the shape)")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="untimed replays of the captured graph for this long before the "
+                         "timed replay, so that it runs at the steady-state clock (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables it)")
     ap.add_argument("--no-reference", action="store_true",
@@ -77,10 +90,10 @@ def sources_sha256(paths) -> str:
     return h.hexdigest()
 
 
-def profile_record(name: str, path_src: str, workload: str):
+def profile_record(name: str, path_src: str, workload: str, shape):
     """The committed counter summary profiles/<name>.json, if it was taken
-    on the current kernel source and headers and on this workload; else
-    None."""
+    on the current kernel source and headers and on this workload and shape
+    [T, K, N]; else None."""
     f = os.path.join(ROOT, "profiles", f"{name}.json")
     if not os.path.exists(f):
         return None
@@ -91,27 +104,32 @@ def profile_record(name: str, path_src: str, workload: str):
         return None
     if os.path.relpath(path_src, ROOT) not in files or rec.get("workload_name") != workload:
         return None
+    if rec.get("shape") != list(shape):
+        return None
     return rec
 
 
-def kernel_traffic(kind: str, path_src: str, workload: str):
-    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE
-    scaled by a copy of known size) from profiles/<kind>_hbm_traffic.json."""
-    rec = profile_record(f"{kind}_hbm_traffic", path_src, workload)
+def kernel_traffic(kernel: str, path_src: str, workload: str, shape):
+    """HBM-side bytes per launch of the dominant kernel (FETCH_SIZE +
+    WRITE_SIZE scaled by a copy of known size) from
+    profiles/<kernel>_<workload>_hbm_traffic.json."""
+    rec = profile_record(f"{kernel}_{workload}_hbm_traffic", path_src, workload, shape)
     return rec.get("bytes_per_launch") if rec else None
 
 
-def clock_adjusted(path_src: str, workload: str, achieved: float):
+def clock_adjusted(path_src: str, workload: str, shape, achieved: float):
     """The int8 peak at the shader clock the GEMM ran at in the committed
     counter run (SQ_BUSY_CYCLES per shader engine over the launch time,
-    profiles/gemm_sclk.json), and the fraction of it achieved here."""
-    rec = profile_record("gemm_sclk", path_src, workload)
+    profiles/k_gemm_<workload>_sclk.json), and the fraction of it achieved
+    here."""
+    name = f"k_gemm_{workload}_sclk"
+    rec = profile_record(name, path_src, workload, shape)
     if not rec:
         return None
     ghz = float(rec["sclk_ghz"])
     peak = PEAK_INT8_TOPS * ghz / 2.4
     return {"sclk_ghz": ghz, "peak": round(peak, 1), "frac": round(achieved / peak, 4),
-            "sclk_from": "profiles/gemm_sclk.json: SQ_BUSY_CYCLES per shader engine over the "
+            "sclk_from": f"profiles/{name}.json: SQ_BUSY_CYCLES per shader engine over the "
                          "profiled k_gemm launches (the 5.0 POP/s peak assumes 2.4 GHz)"}
 
 
@@ -205,11 +223,15 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
+    shape = {}
+    if args.shape:
+        shape = dict(zip("TKN", (int(v) for v in args.shape.split(","))))
+        w = dataclasses.replace(w, **shape)
     thr = w.threshold if args.threshold is None else args.threshold
     T, K, N = w.T, w.K, w.N
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    X_np, W_np, _ = workloads.make(args.workload)
+    X_np, W_np, _ = workloads.make(args.workload, **shape)
     X0 = torch.from_numpy(X_np).to(dev)
     W0 = torch.from_numpy(W_np).to(dev)
     s_inv = None
@@ -222,12 +244,14 @@ def main():
     else:
         Wq0, sW0 = li8.quantize_weight(W0)
 
-    # Buffer sets: one (warm: the call's operands stay in the caches between
-    # calls), or with --cold enough copies that the calls of a cycle touch
+    # Buffer sets.  Warm: one set, so the call's operands stay in the caches
+    # between calls.  Cold: enough copies that the calls of a cycle touch
     # more than twice the 256 MB Infinity Cache, so every call reads its
-    # weight and activations from HBM.
+    # weight and activations from HBM.  Both are measured; `value` is the
+    # warm one unless --cold.
     touched = 2 * T * K + N * K + 2 * T * N + T * K + 4 * (T + N)
-    nsets = max(2, -(-2 * 256 * 2**20 // touched)) if args.cold else 1
+    ncold = max(2, -(-2 * 256 * 2**20 // touched))
+    nsets = ncold if args.cold else 1      # the sets of the primary measurement
 
     def new_set(first):
         st_ = dict(X=X0 if first else X0.clone(), Wq=Wq0 if first else Wq0.clone(),
@@ -240,7 +264,7 @@ def main():
             st_["cache"] = li8.new_cache(K, N, dev)
         return st_
 
-    sets = [new_set(i == 0) for i in range(nsets)]
+    sets = [new_set(i == 0) for i in range(ncold)]
     X, W, Wq, sW, ws, Y = X0, W0, Wq0, sW0, sets[0]["ws"], sets[0]["Y"]
     torch.cuda.synchronize()
 
@@ -282,14 +306,14 @@ def main():
         def gemm(b):
             li8.gemm(b["Wq"], b["sW"], T, b["ws"], out=b["Y"])
 
-    for i in range(max(args.warmup, nsets)):
-        call(sets[i % nsets])
+    for i in range(max(args.warmup, ncold)):
+        call(sets[i % ncold])
     torch.cuda.synchronize()
     y_eager = Y.clone()
 
-    def capture(fn, reps):
+    def capture(fn, reps, nuse):
         """A HIP graph of `reps` back-to-back calls of fn, cycling over the
-        buffer sets (no allocation inside)."""
+        first `nuse` buffer sets (no allocation inside)."""
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -299,38 +323,53 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for r in range(reps):
-                fn(sets[r % nsets])
+                fn(sets[r % nuse])
         torch.cuda.synchronize()
         return g
 
-    def same_as_eager(what):
-        for b in sets:
+    def same_as_eager(what, nuse):
+        for b in sets[:nuse]:
             if not torch.equal(b["Y"].view(torch.int16), y_eager.view(torch.int16)):
                 raise RuntimeError(f"{what}: graph replay differs from the eager call")
 
-    # The K timed steps are one HIP graph of K calls of the product entry
-    # point, so that the host's per-call launch cost (Python, ctypes) does
-    # not pace a short call; the graph's output is checked against the eager
-    # call before and after timing.
-    g_lin = capture(call, args.steps)
-    for b in sets:
-        b["Y"].zero_()
-    g_lin.replay()
-    torch.cuda.synchronize()
-    if args.steps >= nsets:
-        same_as_eager("linear")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record()
-    g_lin.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    if args.steps >= nsets:
-        same_as_eager("linear (timed)")
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    gpu_ms_step = e0.elapsed_time(e1) / args.steps
+    def timed_calls(nuse):
+        """Wall-clock and HIP-event ms per call of one graph of `steps` calls
+        over `nuse` buffer sets.  The K timed steps are one HIP graph of K
+        calls of the product entry point, so that the host's per-call launch
+        cost (Python, ctypes) does not pace a short call; the graph's output
+        is checked against the eager call before and after timing."""
+        g = capture(call, args.steps, nuse)
+        for b in sets[:nuse]:
+            b["Y"].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if args.steps >= nuse:
+            same_as_eager("linear", nuse)
+        # untimed replays until the GPU has run the graph for settle_ms: the
+        # shader clock ramps over the first ~15 ms of sustained load (a call
+        # at 4096x4096x11008 goes 214 -> 202 -> 190 -> 184 us over the first
+        # four 20-call replays, then stays), and the timed steps are meant
+        # to run at the steady clock, as in a model's forward pass
+        t_s = time.perf_counter()
+        while (time.perf_counter() - t_s) * 1e3 < args.settle_ms:
+            g.replay()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if args.steps >= nuse:
+            same_as_eager("linear (timed)", nuse)
+        del g
+        return (t1 - t0) * 1e3 / args.steps, e0.elapsed_time(e1) / args.steps
+
+    ms_step, gpu_ms_step = timed_calls(nsets)
+    other_n = 1 if args.cold else ncold
+    other_ms, other_gpu_ms = timed_calls(other_n)
 
     # Per-stage times for the roofline, with HIP events on torch's current
     # stream, which is the stream the library launches on.  The tiled GEMM
@@ -341,7 +380,9 @@ def main():
     # For few tokens the GEMM is a ~10 us kernel, which a graph of R
     # gemm-only calls times better than events around eager launches.
     R = min(args.steps, 50)
-    few = li8.few_token_path(T, K)
+    pl = li8.plan(T, K, N)
+    few = pl["path"] in ("few_tokens", "few_tokens_split")
+    split = pl["path"] == "few_tokens_split"
 
     def graph_ms(g):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -355,7 +396,7 @@ def main():
     if few:
         for b in sets:   # (the fused call leaves the workspaces unwritten)
             prep(b)
-        g_gemm = capture(gemm, R)
+        g_gemm = capture(gemm, R, nsets)
         gemm_ms = graph_ms(g_gemm)
         del g_gemm
     else:
@@ -369,10 +410,10 @@ def main():
         torch.cuda.synchronize()
         gemm_ms = sum(a.elapsed_time(b) for a, b in ev) / R
     if R >= nsets:
-        same_as_eager("prepare + gemm")
-    g_prep = capture(prep, R)
+        same_as_eager("prepare + gemm", nsets)
+    g_prep = capture(prep, R, nsets)
     prep_ms = graph_ms(g_prep)
-    del g_lin, g_prep
+    del g_prep
 
     st = li8.export_stages(ws, T, K, N)
     nO = int(st["n_outliers"].cpu()[0])
@@ -382,8 +423,13 @@ def main():
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
     # algorithmic bytes of the prepare stage: detection reads X; quantization
     # reads X, writes Xq, sX and the gathered outlier columns of X; the weight
-    # gather reads and writes nO16 bytes per weight row
-    prep_bytes = 2 * T * K + 2 * T * K + T * K + 4 * T + 2 * T * nO16 + 2 * N * nO16
+    # gather reads and writes nO16 bytes per weight row, unless the tiled GEMM
+    # copies those columns itself (llm_int8_plan's fold range) or the call
+    # runs on a few-token path (its kernels read them by index)
+    gathers = not few and not (args.variant == "int8w" and pl["fold_lo"] < nO <= pl["fold_hi"])
+    prep_bytes = 2 * T * K + 2 * T * K + T * K + 4 * T + 2 * T * nO16
+    if gathers:
+        prep_bytes += 2 * N * nO16
     if args.variant == "cached":
         # the weight gather is skipped on a hit (every timed call)
         prep_bytes = 2 * T * K + 2 * T * K + T * K + 4 * T + 2 * T * nO16
@@ -434,6 +480,19 @@ def main():
                     "kernel": "k_decode (few-token GEMM on the workspace, no outliers)",
                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None}
+    elif split:
+        # three kernels are the whole call (scan of X, split-K int8 MFMA
+        # product, finish); the product streams Wq once.  Timed as the whole
+        # call: the split product's own share is in its kernel trace
+        src = os.path.join(ROOT, "int8_matmul_amd", "csrc", "decode_split.hip")
+        call_bytes = N * K + 2 * T * K + 2 * T * N + 4 * N
+        gbps = call_bytes / (gpu_ms_step * 1e-3) / 1e9
+        roofline = {"bound": "hbm",
+                    "kernel": "the whole call: k_dscan + k_dsplit + k_dfinish (split-K "
+                              "few-token path; k_dsplit streams Wq)",
+                    "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                    "traffic": kernel_traffic("split_call", src, args.workload, (T, K, N)) if args.variant == "int8w" else None}
     elif few:
         # one fused kernel is the whole call; it streams Wq once
         src = os.path.join(ROOT, "int8_matmul_amd", "csrc", "decode.hip")
@@ -444,7 +503,7 @@ def main():
                               "int8 MFMA, outlier MFMA, epilogue)",
                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                    "traffic": kernel_traffic("decode", src, args.workload) if args.variant == "int8w" else None}
+                    "traffic": kernel_traffic("k_decode", src, args.workload, (T, K, N)) if args.variant == "int8w" else None}
     else:
         src = os.path.join(ROOT, "int8_matmul_amd", "csrc", "gemm.hip")
         roofline = {"bound": "mfma",
@@ -452,10 +511,13 @@ def main():
                     "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                     # counters taken on the LLM.int8() call only
-                    "traffic": kernel_traffic("gemm", src, args.workload) if args.variant == "int8w" else None,
-                    "clock_adjusted": (clock_adjusted(src, args.workload, gemm_tops)
+                    "traffic": kernel_traffic("k_gemm", src, args.workload, (T, K, N)) if args.variant == "int8w" else None,
+                    "clock_adjusted": (clock_adjusted(src, args.workload, (T, K, N), gemm_tops)
                                        if args.variant == "int8w" else None)}
 
+    warm_desc = "warm: one buffer set, reused by every call"
+    cold_desc = (f"cold: {ncold} rotating copies of the call's buffers, "
+                 f"{ncold * touched / 1e6:.0f} MB touched per cycle")
     entry = {"sq": "smoothquant_linear", "cached": "llm_int8_linear_cached",
              "fp16w": "llm_int8_linear_fp16w"}.get(args.variant, "llm_int8_linear")
     out = {
@@ -468,13 +530,16 @@ def main():
         "ms_per_step": round(ms_step, 5),
         "gpu_ms_per_step": round(gpu_ms_step, 5),
         "timing": f"one HIP graph of `steps` {entry} calls, wall clock between "
-                  "synchronizations; output checked against an eager call",
+                  "synchronizations; output checked against an eager call; before it, "
+                  f"untimed replays of the same graph for {args.settle_ms:g} ms (the clock "
+                  "ramps over the first ~15 ms of sustained load)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": w.desc, "name": args.workload, "T": T, "K": K, "N": N,
+        "config": {"workload": w.desc if not shape else f"{w.desc}, at T={T} K={K} N={N}",
+                   "name": args.workload, "T": T, "K": K, "N": N,
                    "threshold": None if args.variant == "sq" else thr, "n_outliers": nO,
                    "outlier_weight": ("int8w" if args.variant == "cached" else
                                       args.variant if args.variant != "sq" else None),
@@ -482,12 +547,20 @@ def main():
                    "method": ("SmoothQuant-style W8A8, alpha 0.5" if args.variant == "sq"
                               else "LLM.int8() decomposition"),
                    "parallelism": "single GPU",
-                   "cache_state": (f"cold: {nsets} rotating copies of the call's buffers, "
-                                   f"{nsets * touched / 1e6:.0f} MB touched per cycle"
-                                   if args.cold else "warm: one buffer set")},
+                   "cache_state": cold_desc if args.cold else warm_desc},
         "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
-        "path": ("few-token fused kernel" if few and args.variant != "sq" else
-                 "prepare kernel + few-token GEMM" if few else "prepare kernels + tiled GEMM"),
+        ("warm" if args.cold else "cold"): {
+            "cache_state": warm_desc if args.cold else cold_desc,
+            "value": round(ops / (other_ms * 1e-3) / 1e12, 2),
+            "ms_per_step": round(other_ms, 5),
+            "gpu_ms_per_step": round(other_gpu_ms, 5),
+            "pct_int8_peak": round(100.0 * ops / (other_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2)},
+        "path": ("prepare kernel + few-token GEMM" if few and args.variant == "sq" else
+                 "few-token split-K kernels" if split else
+                 "few-token fused kernel" if few else
+                 f"prepare kernels + tiled GEMM ({pl['tile_m']}x{pl['tile_n']} tiles"
+                 + ("; the GEMM copies the weight's outlier columns)" if (
+                     args.variant == "int8w" and pl["fold_lo"] < nO <= pl["fold_hi"]) else ")")),
         "prepare_us": round(prep_ms * 1e3, 2),
         "gemm_us": round(gemm_ms * 1e3, 2),
         "quant_gbps": round(prep_gbps, 1),

@@ -120,13 +120,22 @@ size_t llm_int8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N);
  *                                a finishing kernel (three launches), and
  *                                llm_int8_gemm the last two on the prepared
  *                                workspace; *tile_m = T, *tile_n = 16.
+ *   *fold_lo, *fold_hi  on the tiled path, a call whose outlier count n has
+ *            fold_lo < n <= fold_hi has its GEMM copy the weight's outlier
+ *            columns out of the K stages it streams, and its prepare kernel
+ *            skips that gather; for other counts the prepare kernel gathers
+ *            them (both 0 when the GEMM never copies them).  This holds for
+ *            llm_int8_linear and llm_int8_prepare + _gemm; the fp16-weight
+ *            and cached calls always gather.  On the few-token paths both
+ *            are 0: their kernels read the outlier columns of Wq by index
+ *            and nothing gathers them.
  * Returns LI8_ERR_SHAPE for an invalid shape, LI8_ERR_INVALID_ARG for a
  * null pointer.
  */
 enum { LI8_PATH_EMPTY = 0, LI8_PATH_FEW_TOKENS = 1, LI8_PATH_TILED = 2,
        LI8_PATH_FEW_TOKENS_SPLIT = 3 };
 li8_status llm_int8_plan(int64_t T, int64_t K, int64_t N, int32_t *path, int32_t *tile_m,
-                         int32_t *tile_n);
+                         int32_t *tile_n, int32_t *fold_lo, int32_t *fold_hi);
 
 /*
  * The whole layer: Y[T,N] = decomposed X[T,K] . W^T.

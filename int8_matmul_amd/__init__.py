@@ -87,7 +87,7 @@ def load_library() -> ctypes.CDLL:
     L.llm_int8_linear_workspace_bytes.restype = sz
     L.llm_int8_linear_workspace_bytes.argtypes = [i64, i64, i64]
     L.llm_int8_plan.restype = ctypes.c_int
-    L.llm_int8_plan.argtypes = [i64, i64, i64, vp, vp, vp]
+    L.llm_int8_plan.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
     L.llm_int8_linear.restype = ctypes.c_int
     L.llm_int8_linear.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp, sz, vp]
     L.llm_int8_linear_noalloc.restype = ctypes.c_int
@@ -192,11 +192,13 @@ PATHS = {0: "empty", 1: "few_tokens", 2: "tiled", 3: "few_tokens_split"}
 
 
 def plan(T: int, K: int, N: int) -> dict:
-    """Which kernels a call of this shape runs: path and output tile."""
-    path, tm, tn = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    _check("llm_int8_plan", load_library().llm_int8_plan(T, K, N, ctypes.byref(path),
-                                                          ctypes.byref(tm), ctypes.byref(tn)))
-    return dict(path=PATHS[path.value], tile_m=tm.value, tile_n=tn.value)
+    """Which kernels a call of this shape runs: path, output tile, and the
+    outlier counts (fold_lo, fold_hi] for which the tiled GEMM copies the
+    weight's outlier columns itself instead of the prepare kernel."""
+    out = [ctypes.c_int32() for _ in range(5)]
+    _check("llm_int8_plan", load_library().llm_int8_plan(T, K, N, *(ctypes.byref(o) for o in out)))
+    path, tm, tn, lo, hi = (o.value for o in out)
+    return dict(path=PATHS[path], tile_m=tm, tile_n=tn, fold_lo=lo, fold_hi=hi)
 
 
 def few_token_path(T: int, K: int) -> bool:

@@ -300,13 +300,14 @@ size_t llm_int8_linear_workspace_bytes(int64_t T, int64_t K, int64_t N)
 }
 
 li8_status llm_int8_plan(int64_t T, int64_t K, int64_t N, int32_t *path, int32_t *tile_m,
-                         int32_t *tile_n)
+                         int32_t *tile_n, int32_t *fold_lo, int32_t *fold_hi)
 {
     li8_status st = check_shape(T, K, N);
     if (st != LI8_OK)
         return st;
-    if (!path || !tile_m || !tile_n)
+    if (!path || !tile_m || !tile_n || !fold_lo || !fold_hi)
         return LI8_ERR_INVALID_ARG;
+    *fold_lo = *fold_hi = 0;
     if (T == 0 || N == 0) {
         *path = LI8_PATH_EMPTY;
         *tile_m = *tile_n = 0;
@@ -320,9 +321,14 @@ li8_status llm_int8_plan(int64_t T, int64_t K, int64_t N, int32_t *path, int32_t
         *tile_n = 16;
     } else {
         const GemmPlan p = gemm_plan(T, K, N);
+        const GatherSkip g = gather_above(T, K, N, false, false);
         *path = LI8_PATH_TILED;
         *tile_m = p.bm;
         *tile_n = p.bn;
+        if (g.hi > g.lo) {
+            *fold_lo = g.lo;
+            *fold_hi = g.hi;
+        }
     }
     return LI8_OK;
 }

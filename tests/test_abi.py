@@ -95,17 +95,28 @@ def test_linear_workspace_bytes(lib):
 
 
 def test_plan(lib):
-    assert li8.plan(8, 4096, 4096) == dict(path="few_tokens", tile_m=8, tile_n=16)
+    few = dict(fold_lo=0, fold_hi=0)
+    assert li8.plan(8, 4096, 4096) == dict(path="few_tokens", tile_m=8, tile_n=16, **few)
     assert li8.plan(0, 4096, 4096)["path"] == "empty"
     p = li8.plan(4096, 4096, 11008)
     assert p["path"] == "tiled" and p["tile_m"] == 256 and p["tile_n"] in (128, 192, 256)
+    # the GEMM copies the weight's outlier columns for 16 < nO <= its capacity
+    cap = {128: 256, 192: 128, 256: 64}
+    assert (p["fold_lo"], p["fold_hi"]) == (16, cap[p["tile_n"]])
+    assert li8.plan(512, 5120, 13824) == dict(path="tiled", tile_m=256, tile_n=128,
+                                              fold_lo=16, fold_hi=256)
+    # not past K = 8192, where the bit set no longer fits the GEMM's LDS copy
+    assert li8.plan(4096, 8208, 4096)["fold_hi"] == 0
     assert li8.plan(17, 16, 16)["path"] == "tiled"
     with pytest.raises(li8.Int8MatmulError):
         li8.plan(16, 24, 16)
-    path = ctypes.c_int32()
-    assert lib.llm_int8_plan(4, 16, 4, ctypes.byref(path), None, ctypes.byref(path)) == INVALID
+    o = [ctypes.c_int32() for _ in range(5)]
+    refs = [ctypes.byref(v) for v in o]
+    for i in range(5):
+        args = refs[:i] + [None] + refs[i + 1:]
+        assert lib.llm_int8_plan(4, 16, 4, *args) == INVALID
     assert li8.few_token_path(16, 8192) and not li8.few_token_path(17, 8192)
-    assert li8.plan(8, 11008, 4096) == dict(path="few_tokens_split", tile_m=8, tile_n=16)
+    assert li8.plan(8, 11008, 4096) == dict(path="few_tokens_split", tile_m=8, tile_n=16, **few)
     assert li8.few_token_path(16, 8208) and li8.plan(16, 8208, 5)["path"] == "few_tokens_split"
 
 
