@@ -258,53 +258,50 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     // ISSUE: request stage kt+NS into the buffer just released; LAST: no
     // next stage.
     // Fold: copy stage kt's outlier columns (landed, in its ring buffer)
-    // into WOT, right after the barrier that made it visible, when this
-    // wave has no LDS read in flight and the MFMAs of the previous k-step
-    // are still running.  Each thread takes XU (rank, row) items and issues
-    // every LDS access whether or not its item exists (absent items store
-    // to a dummy byte of their own), so the LDS operations in flight stay
-    // countable; a stage with more than XU * NT items copies the rest in a
-    // loop.  (Measured: placed after the MFMAs of a k-step, or spread over
-    // the k-steps, these LDS operations compete with the fragment reads
-    // and cost more.)
+    // into WOT.  Each thread reads one (rank, row) item right after the
+    // barrier that made the stage visible, when this wave has no LDS read
+    // in flight, and writes it after the MFMAs of that k-step have issued,
+    // so that the MFMAs do not wait behind the read's latency.  The read and
+    // the write are issued whether or not the item exists (an absent item
+    // re-reads a valid byte and stores to a dummy byte of its own), so the
+    // LDS operations in flight stay countable; a stage with more than NT
+    // items copies the rest in a loop.  (Measured against four items per
+    // thread read and written at once: 13B FFN 69.3 -> 62.9 us per call;
+    // 4096 x 4096 x 11008 with 29 outlier columns 209.9 -> 204.6 us.  Two
+    // or four items per thread with the split were slower on 256-wide
+    // tiles, whose registers are nearly all taken.)
     const int32_t *idx_l = reinterpret_cast<const int32_t *>(lds + PF_IDX);
     const int32_t *wpre_l = reinterpret_cast<const int32_t *>(lds + PF_WPRE);
     int8_t *wot = lds + PF_WO;
     const int nwords = (K + 31) / 32;
-    constexpr int XU = kFoldItems;
-    auto extract = [&](int kt) {
+    int8_t xv = 0;          // the item read
+    int xlo = 0, xn = 0;    // first rank and item count of the stage read
+    auto extract_read = [&](int kt) {
         const int lo = __builtin_amdgcn_readfirstlane(wpre_l[min(KS * kt, nwords)]);
         const int hi = __builtin_amdgcn_readfirstlane(wpre_l[min(KS * kt + KS, nwords)]);
         const int n = (hi - lo) * BN;
         const int8_t *bst = lds + (kt % NS) * SSZ + ASZ;
-        int rk[XU], row[XU], col[XU];
-#pragma unroll
-        for (int u = 0; u < XU; u++) {
-            const int it = min(u * NT + tid, max(n - 1, 0));
-            const int rr = it / BN;
-            row[u] = it - rr * BN;
-            rk[u] = min(lo + rr, CAP - 1);
-            col[u] = idx_l[rk[u]] - kt * BKS;
+        const int it = min(tid, max(n - 1, 0));
+        const int rr = it / BN, row = it - rr * BN;
+        const int c = min(max(idx_l[min(lo + rr, CAP - 1)] - kt * BKS, 0), BKS - 1);
+        xv = bst[row * BKS + (((c >> 4) ^ swz<CPR>(row)) << 4) + (c & 15)];
+        xlo = lo;
+        xn = n;
+    };
+    auto extract_write = [&](int kt) {
+        {
+            const int it = min(tid, max(xn - 1, 0));
+            const int rr = it / BN, row = it - rr * BN, r = min(xlo + rr, CAP - 1);
+            int8_t *dst = tid < xn ? wot + (r >> 4) * (BN * 16) + row * 16 + (r & 15) : lds + PF_DUMMY + tid;
+            *dst = xv;
         }
-        int8_t v[XU];
-#pragma unroll
-        for (int u = 0; u < XU; u++) {
-            const int c = min(max(col[u], 0), BKS - 1);
-            v[u] = bst[row[u] * BKS + (((c >> 4) ^ swz<CPR>(row[u])) << 4) + (c & 15)];
-        }
-#pragma unroll
-        for (int u = 0; u < XU; u++) {
-            const bool ok = u * NT + tid < n;
-            int8_t *dst = ok ? wot + (rk[u] >> 4) * (BN * 16) + row[u] * 16 + (rk[u] & 15)
-                             : lds + PF_DUMMY + tid;
-            *dst = v[u];
-        }
-        if (n > XU * NT) {   // (rare: more than XU * NT / BN outlier columns in one stage)
-            for (int it = XU * NT + tid; it < n; it += NT) {
-                const int rr = it / BN, rw = it - rr * BN, r = lo + rr;
+        if (xn > NT) {   // more than NT / BN outlier columns in this stage
+            const int8_t *bst = lds + (kt % NS) * SSZ + ASZ;
+            for (int it = NT + tid; it < xn; it += NT) {
+                const int rr = it / BN, row = it - rr * BN, r = xlo + rr;
                 const int c = idx_l[r] - kt * BKS;
-                wot[(r >> 4) * (BN * 16) + rw * 16 + (r & 15)] =
-                    bst[rw * BKS + (((c >> 4) ^ swz<CPR>(rw)) << 4) + (c & 15)];
+                wot[(r >> 4) * (BN * 16) + row * 16 + (r & 15)] =
+                    bst[row * BKS + (((c >> 4) ^ swz<CPR>(row)) << 4) + (c & 15)];
             }
         }
     };
@@ -337,8 +334,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                 __builtin_amdgcn_sched_barrier(0);
             } else if constexpr (!LAST) {
                 wait_loads_barrier<WAIT>();   // stage kt+1 landed; stage kt read by all
-                if constexpr (FOLD) {   // stage kt+1 landed: its outlier columns
-                    extract(kt + 1);
+                if constexpr (FOLD) {   // stage kt+1 landed: read its outlier columns
+                    extract_read(kt + 1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if constexpr (ISSUE)
@@ -355,6 +352,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
                         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (FOLD) {   // and write them, behind the MFMAs
+                    extract_write(kt + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             } else {
                 __builtin_amdgcn_sched_barrier(0);
                 mfmas(cur);
@@ -427,8 +428,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     // the main loop, in a second copy with the fold's copies when this
     // call folds (the other copy is the plain loop)
     auto main_loop = [&](auto fold_c) {
-        if constexpr (decltype(fold_c)::value)   // stage 0 landed at the prologue's barrier
-            extract(0);
+        if constexpr (decltype(fold_c)::value) {   // stage 0 landed at the prologue's barrier
+            extract_read(0);
+            extract_write(0);
+        }
         int kt = 0;
         for (; kt + NS < nk; kt++)      // steady state
             stage(kt, WS{}, TT{}, TF{}, fold_c);

@@ -119,7 +119,6 @@ hipError_t launch_cache_reset(char *cache, hipStream_t s);
 // cheap (few columns), and the plain main loop is kept.
 constexpr int kFoldMin = 16;
 constexpr int64_t kFoldMaxK = 8192;
-constexpr int kFoldItems = 4;   // (rank, row) items per thread and K stage copied without a loop
 struct GemmPlan {
     int bm, bn, fold;
 };

@@ -218,7 +218,7 @@ def test_gemm_fold_capacity(T, N, tile_n, cap, which):
     stages it streams through LDS; otherwise the prepare kernel gathers
     them.  Both sides of each limit, the columns spread over K, one in the
     ragged last stage; and 40 columns in one 128-column stage, more than a
-    stage's fixed share of copies (2048 / tile width)."""
+    stage's fixed share of copies (512 / tile width)."""
     K = 1040
     n_out = {"min": 16, "min+1": 17, "cap": cap, "cap+1": cap + 1, "dense stage": 40}[which]
     assert li8.plan(T, K, N) == dict(path="tiled", tile_m=256, tile_n=tile_n,
