@@ -135,7 +135,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm(
     // gather them from Wq, a second read of the weight when the outlier
     // columns are spread over K.  It needs the outlier list and the prefix
     // counts per bit-set word (stage s starts at word 4s).
-    constexpr int CAP = F16W ? 0 : (BN >= 256 ? 64 : BN >= 192 ? 128 : 256);
+    constexpr int CAP = (F16W || BN > 128) ? 0 : 256;
     constexpr int NWMAX = kFoldMaxK / 32;      // bit-set words
     constexpr int PF_SX = NS * SSZ, PF_SW = PF_SX + 4 * BM, PF_XO = PF_SW + 4 * BN;
     constexpr int PF_WO = PF_XO + 32 * BM;     // chunk 0 of the gathered WO, or WOT when folding
@@ -710,13 +710,17 @@ GemmPlan gemm_plan(int64_t T, int64_t K, int64_t N)
     const double cost_mid = 0.75 * 1.15 * (double)((mid + kCUs - 1) / kCUs);
     const double cost_small = 0.5 * 1.35 * (double)((small + kCUs - 1) / kCUs);
     // the most outlier columns the int8 GEMM copies out of its weight
-    // fragments (its CAP), for K <= kFoldMaxK (its LDS copy of the bit set)
+    // stages (its CAP), for K <= kFoldMaxK (its LDS copy of the bit set):
+    // 256 on 128-wide tiles; the wider tiles never copy them (measured
+    // slower than the prepare kernel's gather at every count tried: the
+    // copies cost the 256- and 192-wide main loops 19 and 10 us at about 30
+    // outlier columns, where the gather costs 4-5 us)
     const bool fold_k = K <= kFoldMaxK;
     if (cost_small < cost_big && cost_small <= cost_mid)
         return {256, 128, fold_k ? 256 : 0};
     if (cost_mid < cost_big)
-        return {256, 192, fold_k ? 128 : 0};
-    return {256, 256, fold_k ? 64 : 0};
+        return {256, 192, 0};
+    return {256, 256, 0};
 }
 
 hipError_t launch_gemm(const int8_t *Wq, const float *sW, int64_t T, int64_t K, int64_t N,

@@ -114,10 +114,13 @@ hipError_t launch_cache_reset(char *cache, hipStream_t s);
 
 // Tile shape of the tiled GEMM for a call of this shape (gemm.hip), and
 // fold: the most outlier columns whose weight columns its int8 variant
-// copies out of the weight fragments it multiplies (0: none).  A call with
-// kFoldMin < nO <= fold needs no gathered WO; with fewer the gather is
-// cheap (few columns), and the plain main loop is kept.
-constexpr int kFoldMin = 16;
+// copies out of the weight stages it multiplies (0: none).  A call with
+// kFoldMin < nO <= fold needs no gathered WO; with fewer the prepare
+// kernel's gather is the cheaper (measured on 128-wide tiles at 512 x 5120 x
+// 13824 and fewer tokens: 45.7 against 49.4 us per call at 36 outlier
+// columns, even at 78, 56.0 against 59.5 at 133), and the plain main loop
+// is kept.
+constexpr int kFoldMin = 64;
 constexpr int64_t kFoldMaxK = 8192;
 struct GemmPlan {
     int bm, bn, fold;

@@ -100,11 +100,10 @@ def test_plan(lib):
     assert li8.plan(0, 4096, 4096)["path"] == "empty"
     p = li8.plan(4096, 4096, 11008)
     assert p["path"] == "tiled" and p["tile_m"] == 256 and p["tile_n"] in (128, 192, 256)
-    # the GEMM copies the weight's outlier columns for 16 < nO <= its capacity
-    cap = {128: 256, 192: 128, 256: 64}
-    assert (p["fold_lo"], p["fold_hi"]) == (16, cap[p["tile_n"]])
+    # only 128-wide tiles copy the weight's outlier columns, for 64 < nO <= 256
+    assert p["tile_n"] == 128 or (p["fold_lo"], p["fold_hi"]) == (0, 0)
     assert li8.plan(512, 5120, 13824) == dict(path="tiled", tile_m=256, tile_n=128,
-                                              fold_lo=16, fold_hi=256)
+                                              fold_lo=64, fold_hi=256)
     # not past K = 8192, where the bit set no longer fits the GEMM's LDS copy
     assert li8.plan(4096, 8208, 4096)["fold_hi"] == 0
     assert li8.plan(17, 16, 16)["path"] == "tiled"

@@ -209,21 +209,18 @@ def test_outlier_count_at_gather_capacity(n_out):
     assert o["nO"] == n_out
 
 
-@pytest.mark.parametrize("T,N,tile_n,cap", [(1000, 16300, 256, 64), (1000, 8320, 192, 128),
-                                             (300, 520, 128, 256)])
 @pytest.mark.parametrize("which", ["min", "min+1", "cap", "cap+1", "dense stage"])
-def test_gemm_fold_capacity(T, N, tile_n, cap, which):
-    """With more than 16 and at most cap outlier columns (64, 128, 256 by
-    tile width) the tiled GEMM copies their weight columns out of the K
-    stages it streams through LDS; otherwise the prepare kernel gathers
-    them.  Both sides of each limit, the columns spread over K, one in the
-    ragged last stage; and 40 columns in one 128-column stage, more than a
-    stage's fixed share of copies (512 / tile width)."""
-    K = 1040
-    n_out = {"min": 16, "min+1": 17, "cap": cap, "cap+1": cap + 1, "dense stage": 40}[which]
-    assert li8.plan(T, K, N) == dict(path="tiled", tile_m=256, tile_n=tile_n,
-                                     fold_lo=16, fold_hi=cap)
-    rng = np.random.default_rng(9000 + cap + n_out)
+def test_gemm_fold_capacity(which):
+    """On 128-wide tiles, with more than 64 and at most 256 outlier columns,
+    the tiled GEMM copies their weight columns out of the K stages it
+    streams through LDS; otherwise the prepare kernel gathers them.  Both
+    sides of each limit, the columns spread over K, one in the ragged last
+    stage; and 100 columns in one 128-column stage, more than a stage's
+    share of one copy per thread (512 / 128)."""
+    T, K, N = 300, 1040, 520
+    n_out = {"min": 64, "min+1": 65, "cap": 256, "cap+1": 257, "dense stage": 100}[which]
+    assert li8.plan(T, K, N) == dict(path="tiled", tile_m=256, tile_n=128, fold_lo=64, fold_hi=256)
+    rng = np.random.default_rng(9000 + n_out)
     X = rng.standard_normal((T, K)).astype(np.float32)
     if which == "dense stage":
         cols = np.sort(rng.choice(128, n_out - 1, replace=False) + 256)
@@ -233,8 +230,23 @@ def test_gemm_fold_capacity(T, N, tile_n, cap, which):
     X[:, cols] = rng.choice([-1.0, 1.0], (T, n_out)) * rng.uniform(20, 60, (T, n_out))
     X = X.astype(np.float16)
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
-    g, o = check_full(X, W, 6.0, f"fold capacity {tile_n}: {n_out} outlier columns")
+    g, o = check_full(X, W, 6.0, f"fold capacity: {n_out} outlier columns")
     assert o["nO"] == n_out
+
+
+@pytest.mark.parametrize("T,N,tile_n", [(1000, 16300, 256), (1000, 8320, 192)])
+def test_wide_tiles_gather(T, N, tile_n):
+    """The 192- and 256-wide tiles never copy the weight's outlier columns
+    themselves: with 40 outlier columns the prepare kernel gathers them."""
+    K = 1040
+    assert li8.plan(T, K, N) == dict(path="tiled", tile_m=256, tile_n=tile_n, fold_lo=0, fold_hi=0)
+    rng = np.random.default_rng(9100 + tile_n)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    cols = np.append(np.sort(rng.choice(K - 16, 39, replace=False)), K - 5)
+    X[:, cols] = rng.choice([-1.0, 1.0], (T, 40)) * rng.uniform(20, 60, (T, 40))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = check_full(X.astype(np.float16), W, 6.0, f"wide tile {tile_n}: 40 outlier columns")
+    assert o["nO"] == 40
 
 
 @pytest.mark.parametrize("n_out", [32, 33, 256, 257, 513])
