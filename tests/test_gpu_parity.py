@@ -384,6 +384,36 @@ def test_dirty_workspace(T, K, N):
     assert np.array_equal(out[0][0].view(np.uint16), out[0][1].view(np.uint16))
 
 
+@pytest.mark.parametrize("T,K,N", [(300, 1040, 520), (8, 4096, 300), (8, 11008, 300)])
+def test_dirty_workspace_variants(T, K, N):
+    """The fp16-weight, cached and SmoothQuant-style calls, too, give the
+    same output from a workspace whose every byte is set as from a zeroed
+    one (the cache itself starts empty, as after llm_int8_cache_reset)."""
+    X, W, _ = workloads.make("prefill_7b_ffn_up", T=T, K=K, N=N)
+    Xd, Wd = dev(X), dev(W)
+    Wq, sW = li8.quantize_weight(Wd)
+    s_f, s_inv = li8.smoothquant_factors(li8.smoothquant_column_absmax(Xd),
+                                         li8.smoothquant_column_absmax(Wd), 0.5)
+    Wq_s, sW_s = li8.smoothquant_quantize_weight(Wd, s_f)
+    out = {}
+    for fill in (0, 255):
+        ys = []
+        ws = li8.new_workspace(T, K, N, DEV)
+        ws.fill_(fill)
+        ys.append(li8.linear_fp16w(Xd, Wq, sW, Wd, 6.0, workspace=ws))
+        ws.fill_(fill)
+        cache = li8.new_cache(K, N, DEV)
+        ys.append(li8.linear_cached(Xd, Wq, sW, cache, 6.0, workspace=ws))
+        ws.fill_(fill)
+        ys.append(li8.linear_cached(Xd, Wq, sW, cache, 6.0, workspace=ws))   # a hit
+        ws.fill_(fill)
+        ys.append(li8.smoothquant_linear(Xd, s_inv, Wq_s, sW_s, workspace=ws))
+        out[fill] = [host(y).copy() for y in ys]
+    say(f"case dirty workspace variants {T}x{K}x{N}")
+    for a, b in zip(out[0], out[255]):
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
 @pytest.mark.parametrize("T,K,N,tile_n", [
     (1000, 272, 16300, 256),   # 4 x 64 tiles of 256x256: exactly one round
     (1000, 272, 8320, 192),    # 4 x 44 tiles of 256x192, the last 64 features wide
