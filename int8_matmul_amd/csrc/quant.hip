@@ -614,7 +614,11 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
         default: launch_detect(k_detect<16>); break;
         }
     }
-    const int wrows = 32;
+    // weight rows per gather block: 16 (8 for the fp16 weight, twice the
+    // bytes per column).  Measured against 32: 13B fp16-weight call 80.5 ->
+    // 77.1 us (16) and 76.0 us (8); 8 costs 0.5 us elsewhere, 64 and 128
+    // were slower everywhere.
+    const int wrows = W16 ? 8 : 16;
     const int64_t wblocks = (N + wrows - 1) / wrows;
     const size_t lds = 12 * (size_t)(nw > 0 ? nw : 1);   // bits, prefix, non-zero words
     const int64_t xblocks = (T + kPrepRows - 1) / kPrepRows;
