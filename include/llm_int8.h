@@ -172,7 +172,8 @@ li8_status llm_int8_linear(const void *X, const int8_t *Wq, const float *sW,
  *   - Every call on one GPU uses that GPU's one array, so calls that
  *     overlap on one GPU (two streams, two host threads) race and give
  *     wrong results: order them.  Nothing carries over from one call to
- *     the next; each call clears what must start at zero.
+ *     the next: no kernel reads a word of the array that its call has not
+ *     written first.
  *   - The first call on a device looks the array's address up (a host-side
  *     query, no allocation); a failure there returns LI8_ERR_HIP.
  */
@@ -184,9 +185,11 @@ li8_status llm_int8_linear_noalloc(const void *X, const int8_t *Wq, const float 
 /*
  * First half of llm_int8_linear (steps 1-2 above): outlier detection,
  * token-wise quantization of X, and the gathering of the outlier columns of
- * X and of Wq into compact matrices.  Everything it produces stays in
- * `workspace`, which llm_int8_gemm then consumes.  Arguments as for
- * llm_int8_linear.
+ * X and of Wq into compact matrices (those of Wq only where llm_int8_gemm
+ * does not copy them itself: see llm_int8_plan's fold range, and the
+ * few-token paths, whose kernels read them by index).  Everything it
+ * produces stays in `workspace`, which llm_int8_gemm then consumes.
+ * Arguments as for llm_int8_linear.
  */
 li8_status llm_int8_prepare(const void *X, const int8_t *Wq, float threshold,
                             int64_t T, int64_t K, int64_t N,
