@@ -169,9 +169,16 @@ def cpu_baseline(X, W, w, target_s: float, variant: str, thr: float):
             break
         rows = min(w.T, rows * 4)
     rows = int(min(w.T, max(4, rows * target_s / max(dt, 1e-3))))
-    t0 = time.perf_counter()
-    run(rows)
-    dt = time.perf_counter() - t0
+    # when the whole call is shorter than target_s, it is repeated (up to 3
+    # runs while the total stays near target_s) and the fastest run counts
+    dts = []
+    while True:
+        t0 = time.perf_counter()
+        run(rows)
+        dts.append(time.perf_counter() - t0)
+        if len(dts) >= 3 or sum(dts) + dts[-1] > target_s:
+            break
+    dt = min(dts)
     ops = 2.0 * rows * w.N * w.K
     # the oracle's quantize stage on the whole of X, timed on its own:
     # detection and token quantization (sq: the smoothed token quantization),
@@ -204,7 +211,8 @@ def cpu_baseline(X, W, w, target_s: float, variant: str, thr: float):
         "cores": cores,
         "cpu_model": model,
         "kind": "oracle",
-        "sample": what.format(r=rows, T=w.T) + f" ({rows}x{w.K}x{w.N}); {dt:.1f} s",
+        "sample": what.format(r=rows, T=w.T) + f" ({rows}x{w.K}x{w.N}); "
+                  + (f"fastest of {len(dts)} runs, {dt:.1f} s" if len(dts) > 1 else f"{dt:.1f} s"),
         "quant_gbps": round(qbytes / qdt / 1e9, 3),
         "quant_sample": f"{qwhat} ({T}x{K}); {qdt * 1e3:.1f} ms",
     }
