@@ -526,6 +526,10 @@ def main():
     warm_desc = "warm: one buffer set, reused by every call"
     cold_desc = (f"cold: {ncold} rotating copies of the call's buffers, "
                  f"{ncold * touched / 1e6:.0f} MB touched per cycle")
+    if roofline.get("traffic") is not None:
+        roofline["traffic_what"] = ("bytes per launch past the L2 (FETCH_SIZE + WRITE_SIZE, scaled by a "
+                                    "1 GiB copy; Infinity Cache hits included, so an upper bound on HBM "
+                                    "bytes), from the committed counter run on the current kernel source")
     entry = {"sq": "smoothquant_linear", "cached": "llm_int8_linear_cached",
              "fp16w": "llm_int8_linear_fp16w"}.get(args.variant, "llm_int8_linear")
     out = {
