@@ -122,6 +122,79 @@ __device__ void outlier_columns8(const uint32_t *bits, const int32_t *pre, int n
     }
 }
 
+// Magnitude masks for the 8 binary16 values of a chunk (dword i holds
+// columns 2i and 2i+1): halfword e is 0x7fff where bit e of `skip` is clear
+// and 0 where it is set, so that one AND gives the magnitude of a column
+// outside the outlier set and 0 for one inside it.
+__device__ __forceinline__ uint4 keep_mag_halves8(uint32_t skip)
+{
+    const uint2 kb = keep_bytes8(skip);   // byte e: 0xff kept, 0 skipped
+    // bytes (e, e, e+1, e+1) of the byte masks (v_perm_b32 selects)
+    return make_uint4(__builtin_amdgcn_perm(kb.x, kb.x, 0x01010000u) & 0x7fff7fffu,
+                      __builtin_amdgcn_perm(kb.x, kb.x, 0x03030202u) & 0x7fff7fffu,
+                      __builtin_amdgcn_perm(kb.y, kb.y, 0x01010000u) & 0x7fff7fffu,
+                      __builtin_amdgcn_perm(kb.y, kb.y, 0x03030202u) & 0x7fff7fffu);
+}
+
+// Max magnitude of a chunk's values under the masks of keep_mag_halves8.
+__device__ __forceinline__ uint32_t chunk_max_keep(uint4 v, uint4 km)
+{
+    li8_us2 m = __builtin_elementwise_max(__builtin_bit_cast(li8_us2, v.x & km.x),
+                                          __builtin_bit_cast(li8_us2, v.y & km.y));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(li8_us2, v.z & km.z));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(li8_us2, v.w & km.w));
+    return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// Lane exchange within rows of 16 (DPP control code) folded into a max.
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t keep, uint32_t send)
+{
+    return max(keep, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, CTRL, 0xF, 0xF, false));
+}
+
+// Maxima over the 64 lanes of a wave of TB values per lane (TB = 8 or 16),
+// all at once.  A step at lane distance d takes the n values still held
+// and pairs value i with value i + n/2: lanes whose index has bit d clear
+// keep token i, the others token i + n/2, and each combines its own value
+// with its partner's (a lane whose bit d differs), so every step halves
+// the values held.  After the steps for d = 32 .. 64/TB lane l holds part
+// of the maximum of token l / (64/TB), and the last steps reduce within
+// those groups of 64/TB lanes.  Exchanges: the gfx950 lane swaps for
+// d = 32 and 16 (the swap itself places the two tokens), DPP within rows
+// for the rest (rotate by 8; the half-row mirror, which pairs each lane
+// with one whose bit 2 differs; quad permutations).  Returns the token's
+// maximum in every lane of its group.
+template <int TB>
+__device__ __forceinline__ uint32_t wave_max_tokens(const uint32_t (&v)[TB], int lane)
+{
+    static_assert(TB == 8 || TB == 16, "token slots");
+    uint32_t a[TB / 2], b[TB / 4], c[TB / 8];
+#pragma unroll
+    for (int i = 0; i < TB / 2; i++) {   // lanes 0-31: token i, 32-63: token i + TB/2
+        const auto r = __builtin_amdgcn_permlane32_swap(v[i], v[i + TB / 2], false, false);
+        a[i] = max((uint32_t)r[0], (uint32_t)r[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < TB / 4; i++) {   // rows 0, 2: the first value's token, rows 1, 3: the second's
+        const auto r = __builtin_amdgcn_permlane16_swap(a[i], a[i + TB / 4], false, false);
+        b[i] = max((uint32_t)r[0], (uint32_t)r[1]);
+    }
+    const bool s8 = (lane & 8) != 0;
+#pragma unroll
+    for (int i = 0; i < TB / 8; i++)
+        c[i] = max_dpp<0x128>(s8 ? b[i + TB / 8] : b[i], s8 ? b[i] : b[i + TB / 8]);   // row_ror:8
+    uint32_t m;
+    if constexpr (TB == 16) {
+        const bool s4 = (lane & 4) != 0;
+        m = max_dpp<0x141>(s4 ? c[1] : c[0], s4 ? c[0] : c[1]);   // row_half_mirror
+    } else {
+        m = max_dpp<0x141>(c[0], c[0]);
+    }
+    m = max_dpp<0x4E>(m, m);   // quad_perm [2,3,0,1]
+    return max_dpp<0xB1>(m, m);   // quad_perm [1,0,3,2]
+}
+
 // TB: a compile-time bound on T (8 or 16), so that the per-token loops of
 // the activation work run over T <= 8 slots when that suffices.
 template <bool FUSED, int KB, int TB, bool F16W, bool STORE_ACC>
@@ -250,21 +323,25 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
                 if (lane == 0)
                     ocnt[u * kDWaves + wid] = tot;
             }
+            // row maxima over the chunk's columns outside the outlier set:
+            // masks only in a wave where some lane's chunk holds one (a
+            // wave-uniform branch, no divergence over the 8 columns)
+            if (__ballot(fl[u] != 0u) != 0ull) {
+                const uint4 km = keep_mag_halves8(fl[u]);
 #pragma unroll
-            for (int t = 0; t < TB; t++)
-                rm[t] = max(rm[t], chunk_max(xv[u][t], fl[u]));
+                for (int t = 0; t < TB; t++)
+                    rm[t] = max(rm[t], chunk_max_keep(xv[u][t], km));
+            } else {
+#pragma unroll
+                for (int t = 0; t < TB; t++)
+                    rm[t] = max(rm[t], chunk_max(xv[u][t], 0u));
+            }
         }
-        // all reductions first (they overlap), then the stores
-        uint32_t wm[TB];
-#pragma unroll
-        for (int t = 0; t < TB; t++)
-            wm[t] = wave_max(rm[t]);
-        if (lane < TB) {
-            uint32_t m = wm[0];
-#pragma unroll
-            for (int t = 1; t < TB; t++)
-                m = (lane == t) ? wm[t] : m;
-            rmax[lane * kDWaves + wid] = m;
+        {   // the wave's maxima of all TB tokens at once: token t in lanes
+            // t * 64/TB .. (t+1) * 64/TB - 1
+            const uint32_t m = wave_max_tokens<TB>(rm, lane);
+            if ((lane & (64 / TB - 1)) == 0)
+                rmax[(lane / (64 / TB)) * kDWaves + wid] = m;
         }
         lds_barrier();
         // Every wave derives the token scales itself, lane t for token t:
@@ -283,10 +360,15 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             const float rc = 1.0f / sc;
             if (wid == 0 && lane < kDMaxT)
                 sxl[lane] = sc;
+            // A token with sc = 0 has only zeros outside the outlier set,
+            // whose codes are 0; the pair (1, 1) gives exactly those codes
+            // (and 0 for the masked outlier positions), so the code loop
+            // needs no test per token.
+            const float sq = sc == 0.0f ? 1.0f : sc, rq = sc == 0.0f ? 1.0f : rc;
 #pragma unroll
             for (int t = 0; t < TB; t++) {
-                sx[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), t));
-                rx[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rc), t));
+                sx[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sq), t));
+                rx[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rq), t));
             }
         }
         // nO and the rank of this thread's first outlier column in each pass
@@ -311,8 +393,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
 #pragma unroll
                 for (int t = 0; t < TB; t++)
                     if (t < T) {
-                        const uint2 q = (sx[t] == 0.0f) ? make_uint2(0u, 0u)
-                                                        : token_codes8_keep(xv[u][t], keep, sx[t], rx[t]);
+                        const uint2 q = token_codes8_keep(xv[u][t], keep, sx[t], rx[t]);
                         *reinterpret_cast<uint2 *>(xq + (c >> 1) * QS + 16 * t + 8 * (c & 1)) = q;
                     }
             }
