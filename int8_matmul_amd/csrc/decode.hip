@@ -264,6 +264,51 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     constexpr bool kEarly = !(FUSED && KB > 8 && TB > 8);
     int nO;
     int g_idx = 0;   // workspace path: column of outlier rank tid % 32 (loaded before the weights)
+    // The epilogue's small operands for row group rgc, spread over all 512
+    // threads: thread (r = tid / 32, e = tid % 32) fetches the weight of row
+    // r and the activation of token slot r at outlier rank e, threads 0..15
+    // the column scales.  Unconditional buffer loads (zeros past the ends).
+    // gather_store puts them in LDS copy `par`.
+    auto gather_issue = [&](int rgc, uint32_t &g_w, uint32_t &g_x, uint32_t &g_s) {
+        const int e = tid & 31, r = tid >> 5;
+        int col = 0;
+        if constexpr (FUSED) {
+            if (nO <= kIdxCap) {
+                col = idxl[min(e, kIdxCap - 1)];
+            } else {   // more columns than the LDS list holds
+                int c8[8];
+                outlier_columns8(bits, pre, (K + 31) / 32, nO, e, c8);
+                col = max(c8[0], 0);
+            }
+        } else {
+            col = min(max(g_idx, 0), K - 1);
+        }
+        const int rows = min(kDRows, N - rgc * kDRows);
+        const __amdgpu_buffer_rsrc_t rWg =
+            F16W ? make_rsrc(W16 + (int64_t)rgc * kDRows * K, 2 * rows * K)
+                 : make_rsrc(Wq + (int64_t)rgc * kDRows * K, rows * K);
+        const int wo = r * K + col;
+        const int woff = (e < nO && r < rows) ? (F16W ? 2 * wo : wo) : kOutOfRange;
+        if constexpr (F16W)
+            g_w = __builtin_amdgcn_raw_buffer_load_b16(rWg, woff, 0, 0);
+        else
+            g_w = __builtin_amdgcn_raw_buffer_load_b8(rWg, woff, 0, 0);   // (code byte)
+        // 16-column chunks of XO: rank i of token t at ((i / 16) * T + t) * 16 + i % 16
+        const int xo = FUSED ? r * K + col : ((e >> 4) * T + r) * 16 + (e & 15);
+        const __amdgpu_buffer_rsrc_t rXg = FUSED ? make_rsrc(X, 2 * T * K) : make_rsrc(XO_g, 2 * T * K);
+        g_x = __builtin_amdgcn_raw_buffer_load_b16(rXg, (e < nO && r < T) ? 2 * xo : kOutOfRange, 0, 0);
+        g_s = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(sW, 4 * N),
+                                                   tid < kDRows ? 4 * min(rgc * kDRows + tid, N - 1)
+                                                                : kOutOfRange,
+                                                   0, 0);
+    };
+    auto gather_store = [&](int par, uint32_t g_w, uint32_t g_x, uint32_t g_s) {
+        gwl[par * 16 * 32 + tid] = (uint16_t)g_w;   // [r][e] = tid
+        gxl[par * 16 * 32 + tid] = (uint16_t)g_x;
+        if (tid < kDRows)
+            gsl[par * kDRows + tid] = __builtin_bit_cast(float, g_s);
+    };
+
     if constexpr (FUSED) {
         constexpr int CPT = KB / 8;   // 8-column chunks per thread: K <= 4096*CPT
         static_assert(CPT <= kMaxCpt, "chunks per thread");
@@ -385,19 +430,6 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
             orank[u] += nO + before;
             nO += pass;
         }
-#pragma unroll
-        for (int u = 0; u < CPT; u++) {
-            const int c = tid + u * kDThreads;
-            const uint2 keep = keep_bytes8(fl[u]);   // the chunk's columns are the same for every token
-            if (c < nchunk) {
-#pragma unroll
-                for (int t = 0; t < TB; t++)
-                    if (t < T) {
-                        const uint2 q = token_codes8_keep(xv[u][t], keep, sx[t], rx[t]);
-                        *reinterpret_cast<uint2 *>(xq + (c >> 1) * QS + 16 * t + 8 * (c & 1)) = q;
-                    }
-            }
-        }
         // the ascending list of outlier columns (while it fits in LDS), and
         // the rank of each bit-set word's first column for the rank search
         // past that; each thread writes its own chunks' entries
@@ -415,6 +447,26 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
                 }
             }
         }
+        // (the list and the prefixes for every thread's rank search)
+        lds_barrier();
+        // the first row group's epilogue operands, requested now so that
+        // their latency passes during the code computation
+        uint32_t e_w, e_x, e_s;
+        gather_issue(rg, e_w, e_x, e_s);
+#pragma unroll
+        for (int u = 0; u < CPT; u++) {
+            const int c = tid + u * kDThreads;
+            const uint2 keep = keep_bytes8(fl[u]);   // the chunk's columns are the same for every token
+            if (c < nchunk) {
+#pragma unroll
+                for (int t = 0; t < TB; t++)
+                    if (t < T) {
+                        const uint2 q = token_codes8_keep(xv[u][t], keep, sx[t], rx[t]);
+                        *reinterpret_cast<uint2 *>(xq + (c >> 1) * QS + 16 * t + 8 * (c & 1)) = q;
+                    }
+            }
+        }
+        gather_store(0, e_w, e_x, e_s);
         lds_barrier();
     } else {
         // token codes of the prepared workspace into the LDS layout: up to
@@ -524,50 +576,16 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         }
     };
 
-    auto process = [&](int set, int rgc, int par) {
-        // The epilogue's small operands for this row group, spread over all
-        // 512 threads and requested before the MFMAs (loads complete in
-        // order: the MFMAs wait only for the older weight loads): thread
-        // (r = tid / 32, e = tid % 32) fetches the weight of row r and the
-        // activation of token slot r at outlier rank e, threads 0..15 the
-        // column scales.  Unconditional buffer loads (zeros past the ends);
-        // they go to LDS after the MFMAs, for wave 0 to read after the
-        // reduction barrier.
+    auto process = [&](int set, int rgc, int par, bool gathered) {
+        // The epilogue's small operands (gathered here unless the activation
+        // work already did, for the first row group of the fused variant),
+        // requested before the MFMAs: loads complete in order, so the MFMAs
+        // wait only for the older weight loads.  They go to LDS after the
+        // MFMAs, for wave 0 to read after the reduction barrier.
         const int nb = rgc * kDRows + 4 * kg;   // this lane's first feature
-        uint32_t g_w, g_x, g_s;
-        {
-            const int e = tid & 31, r = tid >> 5;
-            int col = 0;
-            if constexpr (FUSED) {
-                if (nO <= kIdxCap) {
-                    col = idxl[min(e, kIdxCap - 1)];
-                } else {   // more columns than the LDS list holds
-                    int c8[8];
-                    outlier_columns8(bits, pre, (K + 31) / 32, nO, e, c8);
-                    col = max(c8[0], 0);
-                }
-            } else {
-                col = min(max(g_idx, 0), K - 1);
-            }
-            const int rows = min(kDRows, N - rgc * kDRows);
-            const __amdgpu_buffer_rsrc_t rWg =
-                F16W ? make_rsrc(W16 + (int64_t)rgc * kDRows * K, 2 * rows * K)
-                     : make_rsrc(Wq + (int64_t)rgc * kDRows * K, rows * K);
-            const int wo = r * K + col;
-            const int woff = (e < nO && r < rows) ? (F16W ? 2 * wo : wo) : kOutOfRange;
-            if constexpr (F16W)
-                g_w = __builtin_amdgcn_raw_buffer_load_b16(rWg, woff, 0, 0);
-            else
-                g_w = __builtin_amdgcn_raw_buffer_load_b8(rWg, woff, 0, 0);   // (code byte)
-            // 16-column chunks of XO: rank i of token t at ((i / 16) * T + t) * 16 + i % 16
-            const int xo = FUSED ? r * K + col : ((e >> 4) * T + r) * 16 + (e & 15);
-            const __amdgpu_buffer_rsrc_t rXg = FUSED ? make_rsrc(X, 2 * T * K) : make_rsrc(XO_g, 2 * T * K);
-            g_x = __builtin_amdgcn_raw_buffer_load_b16(rXg, (e < nO && r < T) ? 2 * xo : kOutOfRange, 0, 0);
-            g_s = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(sW, 4 * N),
-                                                       tid < kDRows ? 4 * min(rgc * kDRows + tid, N - 1)
-                                                                    : kOutOfRange,
-                                                       0, 0);
-        }
+        uint32_t g_w = 0, g_x = 0, g_s = 0;
+        if (!gathered)
+            gather_issue(rgc, g_w, g_x, g_s);
         // fragment reads 8 at a time ahead of their MFMAs, which alternate
         // between two accumulators (the int32 sums are exact, so splitting
         // the dependency chain changes nothing)
@@ -590,12 +608,10 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // (no scheduling across: the stores below wait for the gathers)
         __builtin_amdgcn_sched_barrier(0);
         acc += acc2;
-        uint16_t *gw = gwl + par * 16 * 32, *gx = gxl + par * 16 * 32;
-        float *gs = gsl + par * kDRows;
-        gw[tid] = (uint16_t)g_w;   // [r][e] = tid
-        gx[tid] = (uint16_t)g_x;
-        if (tid < kDRows)
-            gs[tid] = __builtin_bit_cast(float, g_s);
+        if (!gathered)
+            gather_store(par, g_w, g_x, g_s);
+        const uint16_t *gw = gwl + par * 16 * 32, *gx = gxl + par * 16 * 32;
+        const float *gs = gsl + par * kDRows;
         red[(par * kDWaves + wid) * 64 + lane] = acc;
         lds_barrier();
         if (wid != 0)
@@ -686,21 +702,23 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
 
     // One row group per workgroup (N <= 16 x grid): no next group to load.
     if (NRG <= G) {
-        process(0, rg, 0);
+        process(0, rg, 0, FUSED);
         return;
     }
     // Else two row groups per iteration, so that the register set holding
     // the next group's weights is fixed at compile time; the next group's
     // loads are issued before this group's MFMAs
+    bool first = FUSED;   // (its gathers made during the activation work)
     while (rg < NRG) {
         const int rg1 = rg + G;
         wload(1, rg1);   // zeros past the last group
-        process(0, rg, 0);
+        process(0, rg, 0, first);
+        first = false;
         if (rg1 >= NRG)
             break;
         const int rg2 = rg1 + G;
         wload(0, rg2);
-        process(1, rg1, 1);
+        process(1, rg1, 1, false);
         rg = rg2;
     }
 }
