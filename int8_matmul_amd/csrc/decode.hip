@@ -29,6 +29,14 @@
 //    from X and Wq by column index: the first chunk and the column scales
 //    by all threads before the MFMAs, through LDS), the column scale and
 //    the fp16 store.
+// ROLES (the fused variant for K <= 4096 when every row group has a
+// workgroup of its own): the workgroup has 12 waves.  Waves 0-7 do the
+// activation work; waves 8-11 ("MFMA waves") request the row group's weights
+// into their registers at entry, each for the K shares of two activation
+// waves, and run the int8 MFMAs once the codes are in LDS; wave 0 adds their
+// four partial sums.  A wave that issues its 64 KB share of weight loads
+// stalls at issue while the memory pipeline drains; in waves of their own
+// those stalls no longer hold up the activation work.
 // The variant FUSED = false reads the token codes, scales and outlier
 // columns that the prepare kernels left in the workspace instead of
 // deriving them; everything after that is the same code, so the two
@@ -195,10 +203,72 @@ __device__ __forceinline__ uint32_t wave_max_tokens(const uint32_t (&v)[TB], int
     return max_dpp<0xB1>(m, m);   // quad_perm [1,0,3,2]
 }
 
+// The MFMA waves of the ROLES variant (wave mw = 0..3 of them): the weight
+// rows of the workgroup's row group over the K shares of activation waves
+// 2mw and 2mw+1, 16 loads of 16 bytes per lane, then the int8 MFMAs with the
+// token codes from LDS, the partial sums to red[mw].  The barriers pair with
+// the activation waves' (issue, row maxima, outlier list, codes, reduction):
+// 12 of the weight loads before the row-maxima barrier and the other 4 before
+// the next, a split at which these waves reach each barrier about when the
+// activation waves do.
+template <int KB>
+__device__ __forceinline__ void mfma_wave(const int8_t *__restrict__ Wq, int T, int K, int N,
+                                          const int8_t *lds, v4i *red, int mw, int lane)
+{
+    static_assert(KB == 8, "two shares of 8 k-steps");
+    constexpr int NL = 2 * KB;
+    const int S = (K + 63) / 64;
+    const int QS = 16 * T + 16;
+    const int kg = lane >> 4, tok = lane & 15;
+    const int n = min((int)blockIdx.x * kDRows + (lane & 15), N - 1);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wq, N * K);
+    v4i wr[NL];
+    // load i: share w = 2mw + i / KB, its k-step j = i % KB (zeros past the
+    // share's end, so that a k-step is counted by exactly one share)
+    auto wl = [&](int i) {
+        const int w = 2 * mw + i / KB, j = i % KB;
+        const int s0 = w * S / kDWaves, s1 = (w + 1) * S / kDWaves;
+        const int k = (s0 + j) * 64 + 16 * kg;
+        wr[i] = load_w16(rW, k < min(s1 * 64, K) ? n * K + k : kOutOfRange);
+    };
+    __builtin_amdgcn_s_barrier();   // issue barrier: the activation loads go first
+#pragma unroll
+    for (int i = 0; i < 12; i++)
+        wl(i);
+    lds_barrier();   // row maxima
+#pragma unroll
+    for (int i = 12; i < NL; i++)
+        wl(i);
+    lds_barrier();   // outlier list
+    lds_barrier();   // codes in LDS
+    // every code fragment first (all reads in flight), then the MFMAs.  No
+    // masks: a token slot past T only feeds outputs that are never stored,
+    // and a k-step past a share's end meets zero weights; the addresses stay
+    // inside the code region (k-step < 64, QS <= 272)
+    v4i xf[NL];
+#pragma unroll
+    for (int i = 0; i < NL; i++) {
+        const int w = 2 * mw + i / KB, j = i % KB;
+        const int q = (w * S / kDWaves + j) * 4 + kg;
+        xf[i] = *reinterpret_cast<const v4i *>(lds + q * QS + 16 * tok);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    v4i acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NL; i += 2) {
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wr[i], xf[i], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wr[i + 1], xf[i + 1], acc2, 0, 0, 0);
+    }
+    red[mw * 64 + lane] = acc + acc2;   // (copy 0)
+    lds_barrier();   // reduction
+}
+
 // TB: a compile-time bound on T (8 or 16), so that the per-token loops of
-// the activation work run over T <= 8 slots when that suffices.
-template <bool FUSED, int KB, int TB, bool F16W, bool STORE_ACC>
-__global__ __launch_bounds__(kDThreads) void k_decode(
+// the activation work run over T <= 8 slots when that suffices.  ROLES: see
+// the file comment (launched with 12 waves; only for FUSED, K <= 4096 and a
+// grid of one row group per workgroup).
+template <bool FUSED, int KB, int TB, bool F16W, bool STORE_ACC, bool ROLES>
+__global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
     const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq, const float *__restrict__ sW,
     const uint16_t *__restrict__ W16,
     uint32_t thr_mag, int T, int K, int N,
@@ -224,6 +294,13 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     if (tid < 4)   // read by the lanes whose fragment slot holds no token or no column
         reinterpret_cast<uint32_t *>(lds + kOffZero)[tid] = 0u;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if constexpr (ROLES) {
+        static_assert(FUSED && KB == 8, "the MFMA waves cover K <= 4096 of the fused variant");
+        if (wid >= kDWaves) {
+            mfma_wave<KB>(Wq, T, K, N, lds, red, wid - kDWaves, lane);
+            return;
+        }
+    }
     const int QS = 16 * T + 16;
     const int NRG = (N + kDRows - 1) / kDRows;
     const int G = gridDim.x;
@@ -329,7 +406,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kEarly)   // (rg = blockIdx.x < NRG: the grid is at most NRG)
+        if constexpr (kEarly && !ROLES)   // (rg = blockIdx.x < NRG: the grid is at most NRG)
             wload(0, rg);
         uint32_t fl[CPT];
         int orank[CPT];   // outlier columns before this chunk's, within this wave and pass u
@@ -589,6 +666,11 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // fragment reads 8 at a time ahead of their MFMAs, which alternate
         // between two accumulators (the int32 sums are exact, so splitting
         // the dependency chain changes nothing)
+        if constexpr (ROLES) {   // the MFMA waves hold the products
+            if (wid != 0)
+                return;
+            lds_barrier();   // reduction
+        } else {
         v4i acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
 #pragma unroll
         for (int h = 0; h < KB; h += 8) {
@@ -610,12 +692,13 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         acc += acc2;
         if (!gathered)
             gather_store(par, g_w, g_x, g_s);
-        const uint16_t *gw = gwl + par * 16 * 32, *gx = gxl + par * 16 * 32;
-        const float *gs = gsl + par * kDRows;
         red[(par * kDWaves + wid) * 64 + lane] = acc;
         lds_barrier();
         if (wid != 0)
             return;
+        }
+        const uint16_t *gw = gwl + par * 16 * 32, *gx = gxl + par * 16 * 32;
+        const float *gs = gsl + par * kDRows;
         float swv[4];
 #pragma unroll
         for (int r = 0; r < 4; r++)
@@ -623,7 +706,7 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
         // wave 0: lane holds token tok and features nb .. nb+3
         v4i tot = red[par * kDWaves * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < kDWaves; w++)
+        for (int w = 1; w < (ROLES ? 4 : kDWaves); w++)
             tot += red[(par * kDWaves + w) * 64 + lane];
         if constexpr (STORE_ACC) {
             if (tok < T)
@@ -723,26 +806,43 @@ __global__ __launch_bounds__(kDThreads) void k_decode(
     }
 }
 
-template <bool FUSED, int KB, int TB, bool F16W>
-hipError_t launch_kb(const uint16_t *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
-                     uint32_t thr_mag,
-                     int64_t T, int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
-                     const WsLayout &L, hipStream_t s)
+template <bool FUSED, int KB, int TB, bool F16W, bool ROLES>
+hipError_t launch_roles(const uint16_t *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
+                        uint32_t thr_mag,
+                        int64_t T, int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
+                        const WsLayout &L, hipStream_t s)
 {
     const int nrg = (int)((N + kDRows - 1) / kDRows);
     const dim3 grid((unsigned)(nrg < kDecodeMaxBlocks ? nrg : kDecodeMaxBlocks));
+    const dim3 block(ROLES ? kDThreads + 256 : kDThreads);
     const int32_t *meta = FUSED ? nullptr : reinterpret_cast<const int32_t *>(ws + L.meta);
     const int32_t *idx = FUSED ? nullptr : reinterpret_cast<const int32_t *>(ws + L.idx);
     const float *sX = FUSED ? nullptr : reinterpret_cast<const float *>(ws + L.sX);
     const int8_t *Xq = FUSED ? nullptr : reinterpret_cast<const int8_t *>(ws + L.Xq);
     const uint16_t *XO = FUSED ? nullptr : reinterpret_cast<const uint16_t *>(ws + L.XO);
     if (acc)
-        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, true>), grid, dim3(kDThreads), 0, s, X, Wq,
+        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, true, ROLES>), grid, block, 0, s, X, Wq,
                            sW, W16, thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
     else
-        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, false>), grid, dim3(kDThreads), 0, s, X, Wq,
+        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, false, ROLES>), grid, block, 0, s, X, Wq,
                            sW, W16, thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
     return hipGetLastError();
+}
+
+// The MFMA-wave variant where it applies: the fused kernel with K <= 4096
+// and one row group per workgroup (its waves run no row-group loop).
+template <bool FUSED, int KB, int TB, bool F16W>
+hipError_t launch_kb(const uint16_t *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
+                     uint32_t thr_mag,
+                     int64_t T, int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
+                     const WsLayout &L, hipStream_t s)
+{
+    if constexpr (FUSED && KB == 8)
+        if ((N + kDRows - 1) / kDRows <= kDecodeMaxBlocks)
+            return launch_roles<FUSED, KB, TB, F16W, true>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc,
+                                                           ws, L, s);
+    return launch_roles<FUSED, KB, TB, F16W, false>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc, ws,
+                                                    L, s);
 }
 
 } // namespace
