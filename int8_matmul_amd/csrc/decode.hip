@@ -68,8 +68,7 @@ constexpr int kOffBits = kXqMax;                          // uint32[K/32]
 constexpr int kOffPre = kOffBits + 4 * (kDMaxK / 32);     // int32[K/32]
 constexpr int kOffRmax = kOffPre + 4 * (kDMaxK / 32);     // uint32[16][8]: token-major wave maxima
 constexpr int kOffSx = kOffRmax + 4 * kDWaves * kDMaxT;   // float[16] token scales
-constexpr int kOffZero = kOffSx + 4 * kDMaxT;             // 16 zero bytes (padding fragments)
-constexpr int kOffRed = kOffZero + 4 * kDMaxT;            // v4i[2][8][64]
+constexpr int kOffRed = kOffSx + 4 * kDMaxT;              // v4i[2][8][64]
 constexpr int kIdxCap = 256;                              // outlier columns listed in LDS
 constexpr int kOffIdx = kOffRed + 2 * kDWaves * 64 * 16;  // int32[kIdxCap]
 constexpr int kMaxCpt = kDMaxK / (8 * kDThreads);         // 8-column chunks per thread
@@ -291,8 +290,6 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
     v4i *red = reinterpret_cast<v4i *>(lds + kOffRed);
 
     const int tid = threadIdx.x, lane = tid & 63;
-    if (tid < 4)   // read by the lanes whose fragment slot holds no token or no column
-        reinterpret_cast<uint32_t *>(lds + kOffZero)[tid] = 0u;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     if constexpr (ROLES) {
         static_assert(FUSED && KB == 8, "the MFMA waves cover K <= 4096 of the fused variant");
@@ -663,9 +660,14 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
         uint32_t g_w = 0, g_x = 0, g_s = 0;
         if (!gathered)
             gather_issue(rgc, g_w, g_x, g_s);
-        // fragment reads 8 at a time ahead of their MFMAs, which alternate
-        // between two accumulators (the int32 sums are exact, so splitting
-        // the dependency chain changes nothing)
+        // fragment reads 8 at a time, all in flight ahead of their MFMAs,
+        // which alternate between two accumulators (the int32 sums are
+        // exact, so splitting the dependency chain changes nothing).  No
+        // masks: a token slot past T only feeds outputs that are never
+        // stored, and a k-step past the wave's share or past K meets zero
+        // weights.  The reads stay inside the code region: k-steps below
+        // 8 * KB and token slots below 16 address at most 32 * KB blocks of
+        // at most 272 bytes.
         if constexpr (ROLES) {   // the MFMA waves hold the products
             if (wid != 0)
                 return;
@@ -676,11 +678,11 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
         for (int h = 0; h < KB; h += 8) {
             v4i xf[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) {   // (no token or no column: the zero bytes)
+            for (int j = 0; j < 8; j++) {
                 const int q = (s0 + h + j) * 4 + kg;
-                const bool ok = tok < T && s0 + h + j < s1 && 16 * q < K;
-                xf[j] = *reinterpret_cast<const v4i *>(lds + (ok ? q * QS + 16 * tok : kOffZero));
+                xf[j] = *reinterpret_cast<const v4i *>(lds + q * QS + 16 * tok);
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
                 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbuf[set][h + j], xf[j], acc, 0, 0, 0);
