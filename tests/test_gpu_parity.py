@@ -170,6 +170,11 @@ def test_ragged_shapes(T, K, N, thr):
     (8, 11008, 4096),    # 7B FFN down: K past the few-token kernel's bound
     (1, 13824, 512),     # 13B FFN down, one token
     (16, 28672, 64),     # 70B FFN down width, 16 tokens
+    # the separate MFMA waves (K <= 4096, one row group per workgroup) at
+    # their limits, and just past the row-group limit
+    (16, 4096, 4096),    # 256 row groups, the largest K, 16 tokens
+    (5, 3008, 4000),     # 47 k-steps: shares of 5 and 6, a ragged last row group
+    (8, 4096, 4112),     # 257 row groups: the register-weight path and its loop
 ])
 @pytest.mark.parametrize("thr", [6.0, np.inf, 0.0])
 def test_decode_shapes(T, K, N, thr):
