@@ -27,7 +27,13 @@ namespace li8 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPrepRows = 2;   // token rows per quantization workgroup
+// Token rows per quantization workgroup: 1 up to 1024 rows, else 2.  Every
+// workgroup merges the detection strips' bit sets itself; fewer rows per
+// workgroup mean more workgroups in flight.  Measured prepare stage: 13B
+// (512 rows) 11.0 us with 2 rows, 9.05 with 1; at 2048 and 4096 rows 2 rows
+// beat 1 (12.6 against 13.5 us, 21.0 against 22.0) and 4 (13.2, 22.2).
+constexpr int kPrepRowsMax = 2;
+inline int prep_rows(int64_t T) { return T <= 1024 ? 1 : kPrepRowsMax; }
 
 // Block-wide max of a uint32 (all threads get the result).
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *red)
@@ -214,7 +220,7 @@ __device__ int load_bits_and_scan(const uint32_t *__restrict__ parts, int nparts
 
 // ---------------------------------------------------------------------------
 // Token quantization + outlier gathers.  Blocks [0, xblocks) each quantize
-// kPrepRows token rows; the remaining blocks gather the outlier columns of
+// ROWS token rows; the remaining blocks gather the outlier columns of
 // wrows rows of Wq (or of the fp16 weight W16, in the fp16-weight variant)
 // each.  Every block rebuilds the prefix counts of the bit set in LDS, which
 // gives each outlier column its compact index.
@@ -621,10 +627,14 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
     const int wrows = W16 ? 8 : 16;
     const int64_t wblocks = (N + wrows - 1) / wrows;
     const size_t lds = 12 * (size_t)(nw > 0 ? nw : 1);   // bits, prefix, non-zero words
-    const int64_t xblocks = (T + kPrepRows - 1) / kPrepRows;
+    const int rows = prep_rows(T);
+    const int64_t xblocks = (T + rows - 1) / rows;
     const bool reg = nw <= kBitsPerThread * kThreads, narrow = K / 8 <= 2 * kThreads;
-    auto kp = reg ? (narrow ? k_prepare<kPrepRows, true, 2> : k_prepare<kPrepRows, true, 4>)
-                  : (narrow ? k_prepare<kPrepRows, false, 2> : k_prepare<kPrepRows, false, 4>);
+    auto kp = rows == 1
+                  ? (reg ? (narrow ? k_prepare<1, true, 2> : k_prepare<1, true, 4>)
+                         : (narrow ? k_prepare<1, false, 2> : k_prepare<1, false, 4>))
+                  : (reg ? (narrow ? k_prepare<kPrepRowsMax, true, 2> : k_prepare<kPrepRowsMax, true, 4>)
+                         : (narrow ? k_prepare<kPrepRowsMax, false, 2> : k_prepare<kPrepRowsMax, false, 4>));
     auto launch = [&](auto KP) {
     hipLaunchKernelGGL(KP, dim3((unsigned)(xblocks + wblocks)), dim3(kThreads), lds, s, X, Wq,
                        W16, (int)T, (int)K, (int)N, wrows, skip.lo, skip.hi, part,
