@@ -29,20 +29,26 @@
 //    from X and Wq by column index: the first chunk and the column scales
 //    by all threads before the MFMAs, through LDS), the column scale and
 //    the fp16 store.
-// ROLES (the fused variant for K <= 4096 when every row group has a
-// workgroup of its own): the workgroup has 12 waves.  Waves 0-7 do the
-// activation work; waves 8-11 ("MFMA waves") request the row group's weights
-// into their registers at entry, each for the K shares of two activation
-// waves, and run the int8 MFMAs once the codes are in LDS; wave 0 adds their
-// four partial sums.  A wave that issues its 64 KB share of weight loads
+// MW (MFMA waves, the fused variant for K <= 4096): the workgroup gets MW
+// more waves that request the weights into their registers and run the int8
+// MFMAs once the codes are in LDS; waves 0-7 do the activation work, and
+// wave 0 the epilogue.  A wave that issues its share of the weight loads
 // stalls at issue while the memory pipeline drains; in waves of their own
 // those stalls no longer hold up the activation work.
+//  - MW = 4 (one row group per workgroup): each MFMA wave covers the K
+//    shares of two activation waves; 12 waves.
+//  - MW = 8 (more row groups than workgroups, T <= 8): MFMA wave m covers
+//    share m of every row group of the workgroup, with the weights of two
+//    row groups in flight and the epilogue operands gathered a group ahead;
+//    16 waves of at most 128 registers.
 // The variant FUSED = false reads the token codes, scales and outlier
 // columns that the prepare kernels left in the workspace instead of
 // deriving them; everything after that is the same code, so the two
 // variants give bit-identical results.  F16W: the outlier columns multiply
 // the original fp16 weight W16 (the fp16-weight variant), and the sum is
 // D = fl32(fl32(acc * sX) * sW) + sum_O X * W16.
+#include <type_traits>
+
 #include "li8_internal.h"
 #include "quant_math.h"
 
@@ -202,7 +208,7 @@ __device__ __forceinline__ uint32_t wave_max_tokens(const uint32_t (&v)[TB], int
     return max_dpp<0xB1>(m, m);   // quad_perm [1,0,3,2]
 }
 
-// The MFMA waves of the ROLES variant (wave mw = 0..3 of them): the weight
+// The MFMA waves of the MW = 4 variant (wave mw = 0..3 of them): the weight
 // rows of the workgroup's row group over the K shares of activation waves
 // 2mw and 2mw+1, 16 loads of 16 bytes per lane, then the int8 MFMAs with the
 // token codes from LDS, the partial sums to red[mw].  The barriers pair with
@@ -263,11 +269,10 @@ __device__ __forceinline__ void mfma_wave(const int8_t *__restrict__ Wq, int T, 
 }
 
 // TB: a compile-time bound on T (8 or 16), so that the per-token loops of
-// the activation work run over T <= 8 slots when that suffices.  ROLES: see
-// the file comment (launched with 12 waves; only for FUSED, K <= 4096 and a
-// grid of one row group per workgroup).
-template <bool FUSED, int KB, int TB, bool F16W, bool STORE_ACC, bool ROLES>
-__global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
+// the activation work run over T <= 8 slots when that suffices.  MW: see the
+// file comment (launched with 8 + MW waves).
+template <bool FUSED, int KB, int TB, bool F16W, bool STORE_ACC, int MW>
+__global__ __launch_bounds__(kDThreads + 64 * MW) void k_decode(
     const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq, const float *__restrict__ sW,
     const uint16_t *__restrict__ W16,
     uint32_t thr_mag, int T, int K, int N,
@@ -291,8 +296,10 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if constexpr (ROLES) {
-        static_assert(FUSED && KB == 8, "the MFMA waves cover K <= 4096 of the fused variant");
+    constexpr bool ROLES = MW != 0;   // the MFMA waves hold the products
+    static_assert(MW == 0 || (FUSED && KB == 8), "MFMA waves: the fused variant, K <= 4096");
+    static_assert(MW != 8 || TB == 8, "8 MFMA waves: 16 waves of at most 128 registers");
+    if constexpr (MW == 4) {
         if (wid >= kDWaves) {
             mfma_wave<KB>(Wq, T, K, N, lds, red, wid - kDWaves, lane);
             return;
@@ -304,7 +311,8 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
 
     // ---- this wave's share of K: MFMA k-steps [s0, s1) of 64 columns ----
     const int S = (K + 63) / 64;
-    const int s0 = wid * S / kDWaves, s1 = (wid + 1) * S / kDWaves;
+    const int wsh = wid & (kDWaves - 1);   // (an MFMA wave of MW = 8 takes share wid - 8)
+    const int s0 = wsh * S / kDWaves, s1 = (wsh + 1) * S / kDWaves;
     const int kg = lane >> 4;     // 16-byte group of the k-step this lane supplies
     const int tok = lane & 15;    // token slot (B column) of this lane
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wq, N * K);
@@ -343,8 +351,10 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
     // r and the activation of token slot r at outlier rank e, threads 0..15
     // the column scales.  Unconditional buffer loads (zeros past the ends).
     // gather_store puts them in LDS copy `par`.
-    auto gather_issue = [&](int rgc, uint32_t &g_w, uint32_t &g_x, uint32_t &g_s) {
-        const int e = tid & 31, r = tid >> 5;
+    const int gt = tid & (kDThreads - 1);   // (MW = 8: the MFMA waves gather as threads 0..511)
+    // (the column of rank e is the same for every row group)
+    auto gather_col = [&]() -> int {
+        const int e = gt & 31;
         int col = 0;
         if constexpr (FUSED) {
             if (nO <= kIdxCap) {
@@ -357,10 +367,16 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
         } else {
             col = min(max(g_idx, 0), K - 1);
         }
-        const int rows = min(kDRows, N - rgc * kDRows);
+        return col;
+    };
+    auto gather_at = [&](int rgc, int col, uint32_t &g_w, uint32_t &g_x, uint32_t &g_s) {
+        const int e = gt & 31, r = gt >> 5;
+        // a row group past the last one gathers nothing: an empty buffer
+        // at the last group's rows (every offset out of range, zeros)
+        const int rows = rgc < NRG ? min(kDRows, N - rgc * kDRows) : 0;
+        const int64_t rbase = (int64_t)min(rgc, NRG - 1) * kDRows * K;
         const __amdgpu_buffer_rsrc_t rWg =
-            F16W ? make_rsrc(W16 + (int64_t)rgc * kDRows * K, 2 * rows * K)
-                 : make_rsrc(Wq + (int64_t)rgc * kDRows * K, rows * K);
+            F16W ? make_rsrc(W16 + rbase, 2 * rows * K) : make_rsrc(Wq + rbase, rows * K);
         const int wo = r * K + col;
         const int woff = (e < nO && r < rows) ? (F16W ? 2 * wo : wo) : kOutOfRange;
         if constexpr (F16W)
@@ -372,16 +388,83 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
         const __amdgpu_buffer_rsrc_t rXg = FUSED ? make_rsrc(X, 2 * T * K) : make_rsrc(XO_g, 2 * T * K);
         g_x = __builtin_amdgcn_raw_buffer_load_b16(rXg, (e < nO && r < T) ? 2 * xo : kOutOfRange, 0, 0);
         g_s = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(sW, 4 * N),
-                                                   tid < kDRows ? 4 * min(rgc * kDRows + tid, N - 1)
-                                                                : kOutOfRange,
+                                                   gt < kDRows ? 4 * min(rgc * kDRows + gt, N - 1)
+                                                               : kOutOfRange,
                                                    0, 0);
     };
-    auto gather_store = [&](int par, uint32_t g_w, uint32_t g_x, uint32_t g_s) {
-        gwl[par * 16 * 32 + tid] = (uint16_t)g_w;   // [r][e] = tid
-        gxl[par * 16 * 32 + tid] = (uint16_t)g_x;
-        if (tid < kDRows)
-            gsl[par * kDRows + tid] = __builtin_bit_cast(float, g_s);
+    auto gather_issue = [&](int rgc, uint32_t &g_w, uint32_t &g_x, uint32_t &g_s) {
+        gather_at(rgc, gather_col(), g_w, g_x, g_s);
     };
+    auto gather_store = [&](int par, uint32_t g_w, uint32_t g_x, uint32_t g_s) {
+        gwl[par * 16 * 32 + gt] = (uint16_t)g_w;   // [r][e] = gt
+        gxl[par * 16 * 32 + gt] = (uint16_t)g_x;
+        if (gt < kDRows)
+            gsl[par * kDRows + gt] = __builtin_bit_cast(float, g_s);
+    };
+    // row groups of this workgroup: rg, rg + G, ... (the grid is at most NRG)
+    const int nG = (NRG - (int)blockIdx.x + G - 1) / G;
+
+    if constexpr (MW == 8) {
+        if (wid >= kDWaves) {
+            // MFMA waves: share wsh of every row group of the workgroup, the
+            // weights in registers (two row groups in flight); each row
+            // group's partial sums to red[set] and its epilogue operands,
+            // gathered one group ahead, to copy `set`.  Barriers pair with the
+            // activation waves' (issue, row maxima, outlier list, codes) and
+            // then with wave 0's, one per row group.
+            __builtin_amdgcn_s_barrier();   // issue barrier: the activation loads go first
+            wload(0, rg);
+            lds_barrier();   // row maxima
+            nO = 0;
+#pragma unroll
+            for (int w = 0; w < kDWaves; w++)
+                nO += ocnt[w];
+            wload(1, rg + G);   // (zeros past the last row group)
+            lds_barrier();   // outlier list
+            const int gcol = gather_col();
+            uint32_t c_w, c_x, c_s;
+            gather_at(rg, gcol, c_w, c_x, c_s);
+            lds_barrier();   // codes in LDS
+            // Row group i uses weight set i % 2; two groups per iteration so
+            // that the set is fixed at compile time.  The fragments need no
+            // masks: a token slot past T only feeds outputs that are never
+            // stored, a k-step past the share or past K meets zero weights.
+            auto step = [&](auto set_c, int i) {
+                constexpr int set = decltype(set_c)::value;
+                uint32_t n_w, n_x, n_s;
+                gather_at(rg + (i + 1) * G, gcol, n_w, n_x, n_s);   // (zeros past the last group)
+                // code fragments in two batches of four, each read ahead of
+                // its MFMAs (register budget: 16 waves of at most 128)
+                v4i acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int h = 0; h < KB; h += 4) {
+                    v4i xf[4];
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        xf[j] = *reinterpret_cast<const v4i *>(lds + ((s0 + h + j) * 4 + kg) * QS + 16 * tok);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbuf[set][h + j], xf[j], acc, 0, 0, 0);
+                }
+                wload(set, rg + (i + 2) * G);   // (zeros past the last group)
+                gather_store(set, c_w, c_x, c_s);
+                red[(set * kDWaves + wsh) * 64 + lane] = acc;
+                lds_barrier();   // this row group's partial sums and operands
+                c_w = n_w;
+                c_x = n_x;
+                c_s = n_s;
+            };
+            for (int i = 0; i < nG; i += 2) {
+                step(std::integral_constant<int, 0>{}, i);
+                if (i + 1 >= nG)
+                    break;
+                step(std::integral_constant<int, 1>{}, i + 1);
+            }
+            return;
+        }
+    }
+
 
     if constexpr (FUSED) {
         constexpr int CPT = KB / 8;   // 8-column chunks per thread: K <= 4096*CPT
@@ -525,8 +608,9 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
         lds_barrier();
         // the first row group's epilogue operands, requested now so that
         // their latency passes during the code computation
-        uint32_t e_w, e_x, e_s;
-        gather_issue(rg, e_w, e_x, e_s);
+        uint32_t e_w = 0, e_x = 0, e_s = 0;
+        if constexpr (MW != 8)
+            gather_issue(rg, e_w, e_x, e_s);
 #pragma unroll
         for (int u = 0; u < CPT; u++) {
             const int c = tid + u * kDThreads;
@@ -540,7 +624,8 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
                     }
             }
         }
-        gather_store(0, e_w, e_x, e_s);
+        if constexpr (MW != 8)
+            gather_store(0, e_w, e_x, e_s);
         lds_barrier();
     } else {
         // token codes of the prepared workspace into the LDS layout: up to
@@ -708,7 +793,7 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
         // wave 0: lane holds token tok and features nb .. nb+3
         v4i tot = red[par * kDWaves * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < (ROLES ? 4 : kDWaves); w++)
+        for (int w = 1; w < (MW == 4 ? 4 : kDWaves); w++)
             tot += red[(par * kDWaves + w) * 64 + lane];
         if constexpr (STORE_ACC) {
             if (tok < T)
@@ -785,6 +870,13 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
         }
     };
 
+    if constexpr (MW == 8) {   // wave 0: the epilogue of every row group
+        if (wid != 0)
+            return;
+        for (int i = 0; i < nG; i++)
+            process(0, rg + i * G, i & 1, true);
+        return;
+    }
     // One row group per workgroup (N <= 16 x grid): no next group to load.
     if (NRG <= G) {
         process(0, rg, 0, FUSED);
@@ -808,7 +900,7 @@ __global__ __launch_bounds__(ROLES ? kDThreads + 256 : kDThreads) void k_decode(
     }
 }
 
-template <bool FUSED, int KB, int TB, bool F16W, bool ROLES>
+template <bool FUSED, int KB, int TB, bool F16W, int MW>
 hipError_t launch_roles(const uint16_t *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
                         uint32_t thr_mag,
                         int64_t T, int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
@@ -816,35 +908,41 @@ hipError_t launch_roles(const uint16_t *X, const int8_t *Wq, const float *sW, co
 {
     const int nrg = (int)((N + kDRows - 1) / kDRows);
     const dim3 grid((unsigned)(nrg < kDecodeMaxBlocks ? nrg : kDecodeMaxBlocks));
-    const dim3 block(ROLES ? kDThreads + 256 : kDThreads);
+    const dim3 block(kDThreads + 64 * MW);
     const int32_t *meta = FUSED ? nullptr : reinterpret_cast<const int32_t *>(ws + L.meta);
     const int32_t *idx = FUSED ? nullptr : reinterpret_cast<const int32_t *>(ws + L.idx);
     const float *sX = FUSED ? nullptr : reinterpret_cast<const float *>(ws + L.sX);
     const int8_t *Xq = FUSED ? nullptr : reinterpret_cast<const int8_t *>(ws + L.Xq);
     const uint16_t *XO = FUSED ? nullptr : reinterpret_cast<const uint16_t *>(ws + L.XO);
     if (acc)
-        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, true, ROLES>), grid, block, 0, s, X, Wq,
+        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, true, MW>), grid, block, 0, s, X, Wq,
                            sW, W16, thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
     else
-        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, false, ROLES>), grid, block, 0, s, X, Wq,
+        hipLaunchKernelGGL((k_decode<FUSED, KB, TB, F16W, false, MW>), grid, block, 0, s, X, Wq,
                            sW, W16, thr_mag, (int)T, (int)K, (int)N, meta, idx, sX, Xq, XO, Y, acc);
     return hipGetLastError();
 }
 
-// The MFMA-wave variant where it applies: the fused kernel with K <= 4096
-// and one row group per workgroup (its waves run no row-group loop).
+// The MFMA-wave variants where they apply: the fused kernel with K <= 4096,
+// MW = 4 with one row group per workgroup, MW = 8 with more row groups than
+// workgroups and T <= 8.  (MW = 8 at one row group per workgroup measured
+// slower than MW = 4: 6.9 against 5.8 us at 8x4096x4096.)
 template <bool FUSED, int KB, int TB, bool F16W>
 hipError_t launch_kb(const uint16_t *X, const int8_t *Wq, const float *sW, const uint16_t *W16,
                      uint32_t thr_mag,
                      int64_t T, int64_t K, int64_t N, uint16_t *Y, int32_t *acc, const char *ws,
                      const WsLayout &L, hipStream_t s)
 {
-    if constexpr (FUSED && KB == 8)
+    if constexpr (FUSED && KB == 8) {
         if ((N + kDRows - 1) / kDRows <= kDecodeMaxBlocks)
-            return launch_roles<FUSED, KB, TB, F16W, true>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc,
-                                                           ws, L, s);
-    return launch_roles<FUSED, KB, TB, F16W, false>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc, ws,
-                                                    L, s);
+            return launch_roles<FUSED, KB, TB, F16W, 4>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc,
+                                                        ws, L, s);
+        if constexpr (TB == 8)
+            return launch_roles<FUSED, KB, TB, F16W, 8>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc,
+                                                        ws, L, s);
+    }
+    return launch_roles<FUSED, KB, TB, F16W, 0>(X, Wq, sW, W16, thr_mag, T, K, N, Y, acc, ws,
+                                                L, s);
 }
 
 } // namespace
