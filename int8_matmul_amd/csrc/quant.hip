@@ -34,6 +34,14 @@ constexpr int kThreads = 256;
 // beat 1 (12.6 against 13.5 us, 21.0 against 22.0) and 4 (13.2, 22.2).
 constexpr int kPrepRowsMax = 2;
 inline int prep_rows(int64_t T) { return T <= 1024 ? 1 : kPrepRowsMax; }
+// One wave per token row (k_prepare_rows) instead of k_prepare: from 2048
+// rows (below that k_prepare's one row per workgroup keeps more of the chip
+// busy), for K <= 4096 (8 chunks per lane) and X under 2 GiB (buffer
+// offsets).
+inline bool prep_wave_rows(int64_t T, int64_t K)
+{
+    return T >= 2048 && K >= 16 && K <= 4096 && 2 * T * K < ((int64_t)1 << 31);
+}
 
 // Block-wide max of a uint32 (all threads get the result).
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *red)
@@ -226,6 +234,146 @@ __device__ int load_bits_and_scan(const uint32_t *__restrict__ parts, int nparts
 // gives each outlier column its compact index.
 // ---------------------------------------------------------------------------
 
+// The weight-gather part of the prepare kernels: block wb (of the blocks
+// past the token blocks) copies the outlier columns of weight rows
+// [wb*wrows, wb*wrows + wrows) into WO, and block 0 of them writes the
+// outlier list, the count, the prefix counts per bit-set word and the
+// merged bit set.  bits/pre: the merged bit set and its exclusive prefix
+// counts in LDS (nw words each, followed by nw words of scratch).
+template <int NT>
+__device__ __forceinline__ void gather_block(
+    int wb, const int8_t *__restrict__ Wq, const uint16_t *__restrict__ W16, int K, int N,
+    int wrows, int fold_lo, int fold_hi, int nO, const uint32_t *bits, int32_t *pre,
+    uint32_t *__restrict__ bits_g, int32_t *__restrict__ meta, int32_t *__restrict__ idx_g,
+    int32_t *__restrict__ wpre, int8_t *__restrict__ WO, int32_t *__restrict__ cache_hdr,
+    uint32_t *__restrict__ cache_bits, int *nnz_s_p, int *miss_s_p)
+{
+    const int tid = threadIdx.x;
+    const int nw = (K + 31) / 32;
+    const int nO16 = (nO + 15) & ~15;
+    int &nnz_s = *nnz_s_p, &miss_s = *miss_s_p;
+    const int n0 = wb * wrows;
+    const int n1 = min(N, n0 + wrows);
+    if (wb == 0) {
+        for (int w = tid; w < nw; w += NT) {
+            uint32_t b = bits[w];
+            int p = pre[w];
+            while (b) {
+                idx_g[p++] = 32 * w + __ffs(b) - 1;
+                b &= b - 1u;
+            }
+        }
+        if (tid == 0)
+            meta[0] = nO;
+        // outlier columns before each bit-set word (the tiled GEMM's fold),
+        // and the merged bit set (for the cache's record and the stage export)
+        for (int w = tid; w <= nw; w += NT) {
+            wpre[w] = w < nw ? pre[w] : nO;
+            if (w < nw)
+                bits_g[w] = bits[w];
+        }
+    }
+    // Outlier-column cache (cache_hdr non-null): WO is the cache's copy of
+    // the gathered columns.  If the cache holds this call's exact set, the
+    // gather is skipped.  Every gather block decides alike (nothing writes
+    // the cached set during this kernel); k_cache_commit, the next kernel,
+    // records the set.
+    bool miss = true;
+    if (cache_hdr) {
+        if (tid == 0)
+            miss_s = cache_hdr[0] != 1;
+        __syncthreads();
+        bool diff = false;
+        for (int w = tid; w < nw; w += NT)
+            diff |= bits[w] != cache_bits[w];
+        if (diff)
+            atomicOr(&miss_s, 1);
+        __syncthreads();
+        miss = miss_s != 0;
+    }
+    // (the tiled GEMM copies the weight's outlier columns itself when
+    // fold_lo < nO <= fold_hi)
+    if (!miss || nO == 0 || (nO > fold_lo && nO <= fold_hi))   // nothing to gather, or the GEMM takes them
+        return;
+    // list the non-zero words once (one wave, ballot compaction), then
+    // visit (row, non-zero word) pairs only
+    int *nzw = reinterpret_cast<int *>(pre + nw);
+    if (tid < 64) {
+        int cnt = 0;
+        for (int base = 0; base < nw; base += 64) {
+            const int w = base + tid;
+            const bool nz = w < nw && bits[w] != 0u;
+            const uint64_t mask = __ballot(nz);
+            if (nz)
+                nzw[cnt + __popcll(mask & ((1ull << tid) - 1ull))] = w;
+            cnt += __popcll(mask);
+        }
+        if (tid == 0)
+            nnz_s = cnt;
+    }
+    __syncthreads();
+    const int nnz = nnz_s;
+    const int pairs = (n1 - n0) * nnz;
+    if (W16) {   // fp16-weight variant: the outlier columns of W, as fp16
+        uint16_t *WO16 = reinterpret_cast<uint16_t *>(WO);
+        for (int p = tid; p < pairs; p += NT) {
+            const int n = n0 + p / nnz;
+            const int w = nzw[p - (p / nnz) * nnz];
+            uint32_t b = bits[w];
+            const uint16_t *src = W16 + (int64_t)n * K + 32 * w;
+            uint32_t hw[16];   // the word's 32 columns, two per register
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (32 * w + 8 * q < K)
+                    v = *reinterpret_cast<const uint4 *>(src + 8 * q);
+                hw[4 * q] = v.x;
+                hw[4 * q + 1] = v.y;
+                hw[4 * q + 2] = v.z;
+                hw[4 * q + 3] = v.w;
+            }
+            // (16-column chunks: rank i of row n at ((i / 16) * N + n) * 16 + i % 16)
+            int i = pre[w];
+            while (b) {
+                const int j = __ffs(b) - 1;
+                WO16[((int64_t)(i >> 4) * N + n) * 16 + (i & 15)] = (uint16_t)((hw[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                i++;
+                b &= b - 1u;
+            }
+        }
+        for (int p = tid; p < (n1 - n0) * 16; p += NT) {
+            const int n = n0 + p / 16, e = p % 16;
+            if (nO + e < nO16)
+                WO16[((int64_t)((nO + e) >> 4) * N + n) * 16 + ((nO + e) & 15)] = 0;
+        }
+        return;
+    }
+    for (int p = tid; p < pairs; p += NT) {
+        const int n = n0 + p / nnz;
+        const int w = nzw[p - (p / nnz) * nnz];
+        uint32_t b = bits[w];
+        const int8_t *src = Wq + (int64_t)n * K + 32 * w;
+        uint4 lo = *reinterpret_cast<const uint4 *>(src);
+        uint4 hi = make_uint4(0, 0, 0, 0);
+        if (32 * w + 16 < K)
+            hi = *reinterpret_cast<const uint4 *>(src + 16);
+        const uint32_t by[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        // (16-column chunks: rank i of row n at ((i / 16) * N + n) * 16 + i % 16)
+        int i = pre[w];
+        while (b) {
+            const int j = __ffs(b) - 1;
+            WO[((int64_t)(i >> 4) * N + n) * 16 + (i & 15)] = (int8_t)((by[j >> 2] >> (8 * (j & 3))) & 0xffu);
+            i++;
+            b &= b - 1u;
+        }
+    }
+    for (int p = tid; p < (n1 - n0) * 16; p += NT) {
+        const int n = n0 + p / 16, e = p % 16;
+        if (nO + e < nO16)
+            WO[((int64_t)((nO + e) >> 4) * N + n) * 16 + ((nO + e) & 15)] = 0;
+    }
+}
+
 // REG: the bit set fits in kBitsPerThread words per thread (K <= 8192).
 // RREG: 16-byte chunks per thread and row kept in registers (2 when K <=
 // 4096, else 4; columns past RREG * 8 * 256 are read again from memory).
@@ -384,127 +532,184 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
     }
 
     // ---- outlier columns of wrows weight rows ----
-    const int wb = blockIdx.x - xblocks;
-    const int n0 = wb * wrows;
-    const int n1 = min(N, n0 + wrows);
-    if (wb == 0) {
-        for (int w = tid; w < nw; w += kThreads) {
-            uint32_t b = bits[w];
-            int p = pre[w];
-            while (b) {
-                idx_g[p++] = 32 * w + __ffs(b) - 1;
-                b &= b - 1u;
-            }
-        }
-        if (tid == 0)
-            meta[0] = nO;
-        // outlier columns before each bit-set word (the tiled GEMM's fold),
-        // and the merged bit set (for the cache's record and the stage export)
-        for (int w = tid; w <= nw; w += kThreads) {
-            wpre[w] = w < nw ? pre[w] : nO;
-            if (w < nw)
-                bits_g[w] = bits[w];
-        }
-    }
-    // Outlier-column cache (cache_hdr non-null): WO is the cache's copy of
-    // the gathered columns.  If the cache holds this call's exact set, the
-    // gather is skipped.  Every gather block decides alike (nothing writes
-    // the cached set during this kernel); k_cache_commit, the next kernel,
-    // records the set.
-    bool miss = true;
-    if (cache_hdr) {
-        if (tid == 0)
-            miss_s = cache_hdr[0] != 1;
-        __syncthreads();
-        bool diff = false;
-        for (int w = tid; w < nw; w += kThreads)
-            diff |= bits[w] != cache_bits[w];
-        if (diff)
-            atomicOr(&miss_s, 1);
-        __syncthreads();
-        miss = miss_s != 0;
-    }
-    // (the tiled GEMM copies the weight's outlier columns itself when
-    // fold_lo < nO <= fold_hi)
-    if (!miss || nO == 0 || (nO > fold_lo && nO <= fold_hi))   // nothing to gather, or the GEMM takes them
-        return;
-    // list the non-zero words once (one wave, ballot compaction), then
-    // visit (row, non-zero word) pairs only
-    int *nzw = reinterpret_cast<int *>(pre + nw);
-    if (tid < 64) {
-        int cnt = 0;
-        for (int base = 0; base < nw; base += 64) {
-            const int w = base + tid;
-            const bool nz = w < nw && bits[w] != 0u;
-            const uint64_t mask = __ballot(nz);
-            if (nz)
-                nzw[cnt + __popcll(mask & ((1ull << tid) - 1ull))] = w;
-            cnt += __popcll(mask);
-        }
-        if (tid == 0)
-            nnz_s = cnt;
-    }
-    __syncthreads();
-    const int nnz = nnz_s;
-    const int pairs = (n1 - n0) * nnz;
-    if (W16) {   // fp16-weight variant: the outlier columns of W, as fp16
-        uint16_t *WO16 = reinterpret_cast<uint16_t *>(WO);
-        for (int p = tid; p < pairs; p += kThreads) {
-            const int n = n0 + p / nnz;
-            const int w = nzw[p - (p / nnz) * nnz];
-            uint32_t b = bits[w];
-            const uint16_t *src = W16 + (int64_t)n * K + 32 * w;
-            uint32_t hw[16];   // the word's 32 columns, two per register
+    gather_block<kThreads>(blockIdx.x - xblocks, Wq, W16, K, N, wrows, fold_lo, fold_hi, nO, bits, pre,
+                           bits_g, meta, idx_g, wpre, WO, cache_hdr, cache_bits, &nnz_s, &miss_s);
+}
+
+// ---------------------------------------------------------------------------
+// Token quantization with one wave per token row (long prompts, K <= 4096).
+// Lane l holds the 16-byte chunks c = l + 64*s (s < CH) of the wave's row,
+// so the masked row maximum is a wave reduction with no LDS round trip and
+// no barrier, and the wave stores the row's codes, scale and outlier values
+// itself.  A workgroup of 4 waves (4 rows) merges the detection strips' bit
+// sets and builds their prefix counts once, with barriers that wait for LDS
+// only, so the rows keep arriving meanwhile.  The blocks past the token
+// blocks gather the weight's outlier columns as in k_prepare.
+// (Measured against k_prepare's two rows per 256-thread workgroup: prepare
+// stage 21.0 -> 19.3 us at 4096 x 4096, 12.3 -> 11.6 us at 2048 x 4096.
+// Several rows per wave with their loads in flight together, 8 or 16 waves
+// per workgroup, and two threads per bit-set word were all slower or the
+// same; at K = 8192 this layout was slower, 35 -> 37 us.)
+// ---------------------------------------------------------------------------
+template <int CH>
+__global__ __launch_bounds__(kThreads) void k_prepare_rows(
+    const uint16_t *__restrict__ X, const int8_t *__restrict__ Wq,
+    const uint16_t *__restrict__ W16, int T, int K, int N,
+    int wrows, int fold_lo, int fold_hi, const uint32_t *__restrict__ parts, int nparts,
+    uint32_t *__restrict__ bits_g, int32_t *__restrict__ meta, int32_t *__restrict__ idx_g, int32_t *__restrict__ wpre,
+    float *__restrict__ sX,
+    int8_t *__restrict__ Xq,
+    uint16_t *__restrict__ XO, int8_t *__restrict__ WO, int32_t *__restrict__ cache_hdr,
+    uint32_t *__restrict__ cache_bits, int xblocks)
+{
+    typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
+    constexpr int NWV = kThreads / 64;
+    static_assert(CH * 8 * 64 / 32 <= kThreads, "one bit-set word per thread");
+    extern __shared__ uint32_t smem[];
+    __shared__ int32_t scan[NWV];
+    __shared__ int nnz_s, miss_s;
+    const int nw = (K + 31) / 32;
+    uint32_t *bits = smem;
+    int32_t *pre = reinterpret_cast<int32_t *>(smem + nw);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nchunk = K / 8;
+    const bool xblock = (int)blockIdx.x < xblocks;
+    const int t = (int)blockIdx.x * NWV + wid;   // this wave's row (< T unless past the end)
+
+    // Loads first, all unconditional: this thread's bit-set word in every
+    // row strip's partial set (strips past nparts re-read the last one),
+    // then the row (buffer loads, the row's offset in the scalar operand;
+    // chunks past K, and every lane of a weight-gather block, use offset
+    // 2^31, past X, which is under 2 GiB on this path).
+    uint32_t bw = 0u;
+    {
+        const int w = min(tid, nw - 1);
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (32 * w + 8 * q < K)
-                    v = *reinterpret_cast<const uint4 *>(src + 8 * q);
-                hw[4 * q] = v.x;
-                hw[4 * q + 1] = v.y;
-                hw[4 * q + 2] = v.z;
-                hw[4 * q + 3] = v.w;
-            }
-            // (16-column chunks: rank i of row n at ((i / 16) * N + n) * 16 + i % 16)
-            int i = pre[w];
-            while (b) {
-                const int j = __ffs(b) - 1;
-                WO16[((int64_t)(i >> 4) * N + n) * 16 + (i & 15)] = (uint16_t)((hw[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-                i++;
-                b &= b - 1u;
-            }
+        for (int y = 0; y < kDetectParts; y++)
+            bw |= parts[min(y, nparts - 1) * nw + w];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 v[CH];
+    {
+        const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(X), (short)0, (int)(2u * (unsigned)T * (unsigned)K), 0x00020000);
+        const int so = __builtin_amdgcn_readfirstlane((int)(2u * (unsigned)min(t, T - 1) * (unsigned)K));
+#pragma unroll
+        for (int s = 0; s < CH; s++) {
+            const int c = lane + 64 * s;
+            v[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rX, (xblock & (c < nchunk)) ? 16 * c : (int)0x80000000, so, 0));
         }
-        for (int p = tid; p < (n1 - n0) * 16; p += kThreads) {
-            const int n = n0 + p / 16, e = p % 16;
-            if (nO + e < nO16)
-                WO16[((int64_t)((nO + e) >> 4) * N + n) * 16 + ((nO + e) & 15)] = 0;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // merged bit set and its exclusive prefix counts in LDS
+    int nO;
+    {
+        const uint32_t b = tid < nw ? bw : 0u;
+        if (tid < nw)
+            bits[tid] = b;
+        const int s = __popc(b);
+        int x = s;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(x, o, 64);
+            if (lane >= o)
+                x += u;
+        }
+        if (lane == 63)
+            scan[wid] = x;
+        lds_barrier();
+        int base = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < NWV; i++) {
+            base += i < wid ? scan[i] : 0;
+            total += scan[i];
+        }
+        if (tid < nw)
+            pre[tid] = base + x - s;
+        nO = total;
+        lds_barrier();
+    }
+
+    if (xblock) {
+        const int nO16 = (nO + 15) & ~15;
+        const bool live = t < T;   // (uniform)
+        // skip masks of this lane's chunks, and which chunk positions hold
+        // an outlier column in any lane (a wave-uniform bit per position:
+        // the masking is a uniform branch with no memory access)
+        uint32_t skipm[CH];
+        uint32_t anym = 0;
+#pragma unroll
+        for (int s = 0; s < CH; s++) {
+            const int c = lane + 64 * s;
+            skipm[s] = c < nchunk ? (bits[c >> 2] >> (8 * (c & 3))) & 0xffu : 0u;
+            anym |= (__ballot(skipm[s] != 0u) != 0ull ? 1u : 0u) << s;
+        }
+        anym = __builtin_amdgcn_readfirstlane(anym);
+        uint32_t m = 0;
+#pragma unroll
+        for (int s = 0; s < CH; s++) {
+            if ((anym >> s) & 1u)
+                m = max(m, masked_max8(v[s], skipm[s]));
+            else
+                m = max(m, chunk_max(v[s], 0u));
+        }
+        m = wave_max(m);
+        const float sc = h2f(m) / 127.0f;
+        const float rc = 1.0f / sc;
+        // a zero scale (every normal value of the row is 0) quantizes with
+        // (1, 1), which gives those zeros their code 0
+        const float su = sc == 0.0f ? 1.0f : sc, ru = sc == 0.0f ? 1.0f : rc;
+        // stores: the row's offset in the scalar operand; a row past T puts
+        // every lane out of range
+        const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(Xq, (short)0, T * K, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(sX, (short)0, 4 * T, 0x00020000);
+        const int so = __builtin_amdgcn_readfirstlane(live ? t * K : 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), rS,
+                                              (live & (lane == 0)) ? 4 * t : (int)0x80000000, 0, 0);
+#pragma unroll
+        for (int s = 0; s < CH; s++) {
+            uint2 q = token_codes8(v[s], 0u, su, ru);
+            if ((anym >> s) & 1u) {
+                const uint2 keep = keep_bytes8(skipm[s]);
+                q.x &= keep.x;
+                q.y &= keep.y;
+            }
+            const int c = lane + 64 * s;
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u_t, q), rQ,
+                                                  (live & (c < nchunk)) ? 8 * c : (int)0x80000000, so, 0);
+        }
+        // outlier values (rank r of row t at ((r / 16) * T + t) * 16 + r % 16),
+        // from the lanes that hold them, then the zero pad
+        if (live) {
+#pragma unroll
+            for (int s = 0; s < CH; s++) {
+                uint32_t sk = skipm[s];
+                if (((anym >> s) & 1u) && sk) {
+                    const int c = lane + 64 * s;
+                    const uint4 x = v[s];
+                    int r = pre[c >> 2] + __popc(bits[c >> 2] & ((1u << (8 * (c & 3))) - 1u));
+#pragma unroll 1
+                    while (sk) {
+                        const int e = __builtin_ctz(sk);
+                        sk &= sk - 1u;
+                        const uint32_t w = e < 4 ? (e < 2 ? x.x : x.y) : (e < 6 ? x.z : x.w);
+                        XO[((int64_t)(r >> 4) * T + t) * 16 + (r & 15)] = (uint16_t)((w >> (16 * (e & 1))) & 0xffffu);
+                        r++;
+                    }
+                }
+            }
+            if (lane < nO16 - nO)
+                XO[((int64_t)((nO + lane) >> 4) * T + t) * 16 + ((nO + lane) & 15)] = 0;
         }
         return;
     }
-    for (int p = tid; p < pairs; p += kThreads) {
-        const int n = n0 + p / nnz;
-        const int w = nzw[p - (p / nnz) * nnz];
-        uint32_t b = bits[w];
-        const int8_t *src = Wq + (int64_t)n * K + 32 * w;
-        uint4 lo = *reinterpret_cast<const uint4 *>(src);
-        uint4 hi = make_uint4(0, 0, 0, 0);
-        if (32 * w + 16 < K)
-            hi = *reinterpret_cast<const uint4 *>(src + 16);
-        const uint32_t by[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        // (16-column chunks: rank i of row n at ((i / 16) * N + n) * 16 + i % 16)
-        int i = pre[w];
-        while (b) {
-            const int j = __ffs(b) - 1;
-            WO[((int64_t)(i >> 4) * N + n) * 16 + (i & 15)] = (int8_t)((by[j >> 2] >> (8 * (j & 3))) & 0xffu);
-            i++;
-            b &= b - 1u;
-        }
-    }
-    for (int p = tid; p < (n1 - n0) * 16; p += kThreads) {
-        const int n = n0 + p / 16, e = p % 16;
-        if (nO + e < nO16)
-            WO[((int64_t)((nO + e) >> 4) * N + n) * 16 + ((nO + e) & 15)] = 0;
-    }
+
+    // ---- outlier columns of wrows weight rows ----
+    gather_block<kThreads>(blockIdx.x - xblocks, Wq, W16, K, N, wrows, fold_lo, fold_hi, nO, bits, pre,
+                           bits_g, meta, idx_g, wpre, WO, cache_hdr, cache_bits, &nnz_s, &miss_s);
 }
 
 // After k_prepare on a cache: the same comparison as its gather blocks
@@ -630,6 +835,24 @@ hipError_t launch_prepare(const uint16_t *X, const int8_t *Wq, const uint16_t *W
     const int rows = prep_rows(T);
     const int64_t xblocks = (T + rows - 1) / rows;
     const bool reg = nw <= kBitsPerThread * kThreads, narrow = K / 8 <= 2 * kThreads;
+    if (prep_wave_rows(T, K)) {   // one wave per token row
+        const int64_t xb = (T + 3) / 4;
+        hipLaunchKernelGGL(k_prepare_rows<8>, dim3((unsigned)(xb + wblocks)), dim3(kThreads), lds, s, X,
+                           Wq, W16, (int)T, (int)K, (int)N, wrows, skip.lo, skip.hi, part,
+                           std::max(dg.gy, 1), bits, meta, reinterpret_cast<int32_t *>(ws + L.idx),
+                           reinterpret_cast<int32_t *>(ws + L.wpre),
+                           reinterpret_cast<float *>(ws + L.sX),
+                           reinterpret_cast<int8_t *>(ws + L.Xq),
+                           reinterpret_cast<uint16_t *>(ws + L.XO),
+                           reinterpret_cast<int8_t *>(cache ? cache + C.WO : ws + L.WO),
+                           cache ? reinterpret_cast<int32_t *>(cache + C.hdr) : nullptr,
+                           cache ? reinterpret_cast<uint32_t *>(cache + C.bits) : nullptr, (int)xb);
+        if (cache)
+            hipLaunchKernelGGL(k_cache_commit, dim3(1), dim3(kThreads), 0, s, bits, meta, nw,
+                               reinterpret_cast<int32_t *>(cache + C.hdr),
+                               reinterpret_cast<uint32_t *>(cache + C.bits));
+        return hipGetLastError();
+    }
     auto kp = rows == 1
                   ? (reg ? (narrow ? k_prepare<1, true, 2> : k_prepare<1, true, 4>)
                          : (narrow ? k_prepare<1, false, 2> : k_prepare<1, false, 4>))

@@ -63,6 +63,7 @@ def batches(T, K, N, sparse=0.0, seed=0):
     (96, 2048, 384, 2e-3),      # hundreds of outlier columns spread over K
     (1000, 4096, 1100, 0.0),
     (1000, 272, 8320, 0.0),     # 256x192 GEMM tiles, the last 64 features wide
+    (2050, 1024, 700, 2e-4),    # one wave per token row in the prepare kernel; 330 outlier columns
 ])
 def test_sequence_hits_misses_and_bits(T, K, N, sparse):
     print(f"case cache sequence {T}x{K}x{N} sparse={sparse}", flush=True)

@@ -85,6 +85,7 @@ def test_tiny(thr):
     (16, 8192, 130),
     (8, 4096, 11008),    # several row groups per workgroup on the few-token path
     (8, 11008, 300),     # few tokens with K past the few-token kernel's bound
+    (2050, 1040, 96),    # one wave per token row in the prepare kernel
 ])
 @pytest.mark.parametrize("thr", [6.0, np.inf, 0.0])
 def test_shapes(T, K, N, thr):

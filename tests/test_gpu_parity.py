@@ -463,3 +463,46 @@ def test_many_tokens_narrow():
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
     g, o = check_full(X, W, 6.0, "many tokens, narrow layer")
     assert o["nO"] == 2
+
+
+# ---------------------------------------------------------------------------
+# Long prompts (from 2048 tokens): with K <= 4096 the token quantization runs
+# one wave per row, four rows per workgroup, and a ragged token count leaves
+# the last workgroup's waves partly past T; a longer K keeps the workgroup per
+# row.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,K,N", [
+    (2048, 4096, 64),    # one wave per row, 8 chunks per lane
+    (2051, 4112, 40),    # K past 4096: a workgroup per row
+    (2050, 272, 520),    # 34 chunks per row: most lanes hold none; last workgroup half past T
+    (8201, 1040, 48),    # 2051 workgroups of rows, the last with one live wave
+    (4096, 8192, 32),    # the 70B slice's K
+])
+@pytest.mark.parametrize("thr", [6.0, np.inf, 0.0])
+def test_long_prompt_rows(T, K, N, thr):
+    w = workloads.WORKLOADS["ffn_13b"]
+    rng = np.random.default_rng(T + 5 * K + 7 * N)
+    X, _ = workloads.make_activation(w, seed=int(rng.integers(1 << 30)), T=T, K=K)
+    W = workloads.make_weight(w, seed=int(rng.integers(1 << 30)), N=N, K=K)
+    check_full(X, W, thr, f"long prompt {T}x{K}x{N}")
+
+
+def test_long_prompt_special_rows():
+    """Rows whose scale is 0 (all zero; only outlier values) and many
+    outlier columns spread over K, on the one-wave-per-row path (the last
+    row, 2049, is the second wave of the last workgroup, whose other two
+    waves are past T)."""
+    T, K, N = 2050, 4096, 48
+    rng = np.random.default_rng(41)
+    X = np.clip(rng.standard_normal((T, K)), -5.0, 5.0).astype(np.float32)
+    cols = np.sort(rng.choice(K, 300, replace=False))
+    X[rng.integers(4, T - 1, 300), cols] = rng.choice([-1.0, 1.0], 300) * rng.uniform(7, 60, 300)
+    X[3, :] = 0.0
+    X[2049, :] = 0.0
+    X[2049, cols[:5]] = 25.0
+    X = X.astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = check_full(X, W, 6.0, "long prompt, zero-scale rows, 300 outlier columns")
+    assert o["nO"] == 300
+    assert g["sX"][3] == 0 and g["sX"][2049] == 0
