@@ -536,6 +536,18 @@ __global__ __launch_bounds__(kThreads) void k_prepare(
                            bits_g, meta, idx_g, wpre, WO, cache_hdr, cache_bits, &nnz_s, &miss_s);
 }
 
+// v with the binary16 values whose bit in skip is set replaced by +0.
+__device__ __forceinline__ uint4 clear_halves8(uint4 v, uint32_t skip)
+{
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t b = ((skip >> (2 * i)) & 1u) | (((skip >> (2 * i + 1)) & 1u) << 16);
+        w[i] &= ~(b * 0xffffu);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ---------------------------------------------------------------------------
 // Token quantization with one wave per token row (long prompts, K <= 4096).
 // Lane l holds the 16-byte chunks c = l + 64*s (s < CH) of the wave's row,
@@ -584,10 +596,13 @@ __global__ __launch_bounds__(kThreads) void k_prepare_rows(
     // 2^31, past X, which is under 2 GiB on this path).
     uint32_t bw = 0u;
     {
-        const int w = min(tid, nw - 1);
+        // (the strip's offset in the scalar operand)
+        const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(parts), (short)0, 4 * nparts * nw, 0x00020000);
+        const int vo = 4 * min(tid, nw - 1);
 #pragma unroll
         for (int y = 0; y < kDetectParts; y++)
-            bw |= parts[min(y, nparts - 1) * nw + w];
+            bw |= __builtin_amdgcn_raw_buffer_load_b32(rP, vo, 4 * min(y, nparts - 1) * nw, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     uint4 v[CH];
@@ -648,39 +663,6 @@ __global__ __launch_bounds__(kThreads) void k_prepare_rows(
             anym |= (__ballot(skipm[s] != 0u) != 0ull ? 1u : 0u) << s;
         }
         anym = __builtin_amdgcn_readfirstlane(anym);
-        uint32_t m = 0;
-#pragma unroll
-        for (int s = 0; s < CH; s++) {
-            if ((anym >> s) & 1u)
-                m = max(m, masked_max8(v[s], skipm[s]));
-            else
-                m = max(m, chunk_max(v[s], 0u));
-        }
-        m = wave_max(m);
-        const float sc = h2f(m) / 127.0f;
-        const float rc = 1.0f / sc;
-        // a zero scale (every normal value of the row is 0) quantizes with
-        // (1, 1), which gives those zeros their code 0
-        const float su = sc == 0.0f ? 1.0f : sc, ru = sc == 0.0f ? 1.0f : rc;
-        // stores: the row's offset in the scalar operand; a row past T puts
-        // every lane out of range
-        const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(Xq, (short)0, T * K, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(sX, (short)0, 4 * T, 0x00020000);
-        const int so = __builtin_amdgcn_readfirstlane(live ? t * K : 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), rS,
-                                              (live & (lane == 0)) ? 4 * t : (int)0x80000000, 0, 0);
-#pragma unroll
-        for (int s = 0; s < CH; s++) {
-            uint2 q = token_codes8(v[s], 0u, su, ru);
-            if ((anym >> s) & 1u) {
-                const uint2 keep = keep_bytes8(skipm[s]);
-                q.x &= keep.x;
-                q.y &= keep.y;
-            }
-            const int c = lane + 64 * s;
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u_t, q), rQ,
-                                                  (live & (c < nchunk)) ? 8 * c : (int)0x80000000, so, 0);
-        }
         // outlier values (rank r of row t at ((r / 16) * T + t) * 16 + r % 16),
         // from the lanes that hold them, then the zero pad
         if (live) {
@@ -703,6 +685,37 @@ __global__ __launch_bounds__(kThreads) void k_prepare_rows(
             }
             if (lane < nO16 - nO)
                 XO[((int64_t)((nO + lane) >> 4) * T + t) * 16 + ((nO + lane) & 15)] = 0;
+        }
+        // then the outlier values are cleared in registers: the row maximum
+        // over the rest is the plain maximum, and a cleared value gets code
+        // 0, the code of an outlier column
+#pragma unroll
+        for (int s = 0; s < CH; s++)
+            if ((anym >> s) & 1u)
+                v[s] = clear_halves8(v[s], skipm[s]);
+        uint32_t m = 0;
+#pragma unroll
+        for (int s = 0; s < CH; s++)
+            m = max(m, chunk_max(v[s], 0u));
+        m = wave_max(m);
+        const float sc = h2f(m) / 127.0f;
+        const float rc = 1.0f / sc;
+        // a zero scale (every normal value of the row is 0) quantizes with
+        // (1, 1), which gives those zeros their code 0
+        const float su = sc == 0.0f ? 1.0f : sc, ru = sc == 0.0f ? 1.0f : rc;
+        // stores: the row's offset in the scalar operand; a row past T puts
+        // every lane out of range
+        const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(Xq, (short)0, T * K, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(sX, (short)0, 4 * T, 0x00020000);
+        const int so = __builtin_amdgcn_readfirstlane(live ? t * K : 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), rS,
+                                              (live & (lane == 0)) ? 4 * t : (int)0x80000000, 0, 0);
+#pragma unroll
+        for (int s = 0; s < CH; s++) {
+            const uint2 q = token_codes8(v[s], 0u, su, ru);
+            const int c = lane + 64 * s;
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u_t, q), rQ,
+                                                  (live & (c < nchunk)) ? 8 * c : (int)0x80000000, so, 0);
         }
         return;
     }
