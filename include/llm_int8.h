@@ -390,6 +390,39 @@ li8_status llm_int8_export_stages(const void *workspace, size_t workspace_bytes,
                                   int32_t *outlier_idx, int8_t *Xq, float *sX,
                                   void *X_out, hipStream_t stream);
 
+/*
+ * Every intermediate result of one linear call, for tests: the rows of the
+ * method one by one (hncyxsy.com/news/230290, section 2.1: the outlier
+ * columns, the vector-wise int8 quantization of the rest and their int8
+ * product, the fp16 product of the outlier columns; tqpw.cn/news/5683,
+ * section 2.1: scale and codes).  It runs llm_int8_prepare and
+ * llm_int8_gemm on `workspace` (the kernels of llm_int8_linear on the tiled
+ * path; on the few-token paths the two-call route, whose Y equals the
+ * one-call kernel's bit for bit), writes Y, and copies out:
+ *   flags        [K] uint8: 1 if column j is an outlier column, else 0.
+ *   n_outliers   [1] int32: nO, the number of outlier columns.
+ *   outlier_idx  [K] int32: the outlier columns in ascending order;
+ *                entries from nO on are unspecified.
+ *   Xq           [T,K] int8: token codes (0 in outlier columns).
+ *   sX           [T] fp32: token scales.
+ *   X_out        [T,K] fp16, row stride K: X[t, outlier_idx[i]] at
+ *                t*K + i for i < nO; the rest of each row is unspecified.
+ *   acc          [T,N] int32: the exact int8 sums, as llm_int8_gemm's acc.
+ * Any of these output pointers may be NULL (that output is skipped).  The
+ * other arguments are those of llm_int8_linear; the workspace must be at
+ * least llm_int8_workspace_bytes(T, K, N) (it is the int8 layout of
+ * llm_int8_prepare).  Outputs are device memory owned by the caller.
+ * Errors as for llm_int8_prepare and llm_int8_gemm, from host checks made
+ * before anything is enqueued; LI8_ERR_ALIGN also for a misaligned Xq, sX,
+ * X_out or acc.
+ */
+li8_status llm_int8_stages(const void *X, const int8_t *Wq, const float *sW,
+                           float threshold, int64_t T, int64_t K, int64_t N,
+                           void *Y, void *workspace, size_t workspace_bytes,
+                           uint8_t *flags, int32_t *n_outliers,
+                           int32_t *outlier_idx, int8_t *Xq, float *sX,
+                           void *X_out, int32_t *acc, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

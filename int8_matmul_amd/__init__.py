@@ -30,7 +30,7 @@ __all__ = [
     "Int8MatmulError", "LibraryNotBuilt", "library_path", "load_library",
     "quantize_weight", "workspace_bytes", "linear_workspace_bytes", "plan", "new_workspace",
     "linear", "linear_noalloc", "NOALLOC_SCRATCH_BYTES", "prepare",
-    "gemm", "export_stages", "few_token_path", "linear_fp16w", "prepare_fp16w",
+    "gemm", "export_stages", "stages", "few_token_path", "linear_fp16w", "prepare_fp16w",
     "gemm_fp16w", "smoothquant_column_absmax", "smoothquant_factors",
     "smoothquant_quantize_weight", "smoothquant_prepare", "smoothquant_linear",
     "cache_bytes", "new_cache", "cache_reset", "cache_stats", "linear_cached", "prepare_cached",
@@ -127,6 +127,9 @@ def load_library() -> ctypes.CDLL:
     L.llm_int8_gemm_cached.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, sz, vp, sz, vp]
     L.llm_int8_export_stages.restype = ctypes.c_int
     L.llm_int8_export_stages.argtypes = [vp, sz, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.llm_int8_stages.restype = ctypes.c_int
+    L.llm_int8_stages.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp, sz, vp, vp, vp,
+                                  vp, vp, vp, vp, vp]
     _lib = L
     return L
 
@@ -553,4 +556,33 @@ def export_stages(workspace: torch.Tensor, T: int, K: int, N: int) -> dict:
                                     _ptr(r["outlier_bits"]), _ptr(r["n_outliers"]),
                                     _ptr(r["outlier_idx"]), _ptr(r["Xq"]), _ptr(r["sX"]),
                                     _ptr(r["X_out"]), _stream(dev)))
+    return r
+
+
+def stages(X: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, threshold: float,
+           workspace: torch.Tensor | None = None) -> dict:
+    """Y and every intermediate result of one call (llm_int8_stages)."""
+    L = load_library()
+    _require(X, torch.float16, "X", 2)
+    _require(Wq, torch.int8, "Wq", 2)
+    _require(sW, torch.float32, "sW", 1)
+    T, K = X.shape
+    N = Wq.shape[0]
+    dev = X.device
+    ws = _ws(workspace, T, K, N, dev)
+    r = dict(
+        Y=torch.empty((T, N), dtype=torch.float16, device=dev),
+        flags=torch.empty(max(K, 1), dtype=torch.uint8, device=dev),
+        n_outliers=torch.empty(1, dtype=torch.int32, device=dev),
+        outlier_idx=torch.empty(max(K, 1), dtype=torch.int32, device=dev),
+        Xq=torch.empty((T, K), dtype=torch.int8, device=dev),
+        sX=torch.empty(max(T, 1), dtype=torch.float32, device=dev),
+        X_out=torch.empty((T, K), dtype=torch.float16, device=dev),
+        acc=torch.empty((T, N), dtype=torch.int32, device=dev),
+    )
+    _check("llm_int8_stages",
+           L.llm_int8_stages(_ptr(X), _ptr(Wq), _ptr(sW), float(threshold), T, K, N, _ptr(r["Y"]),
+                             _ptr(ws), ws.numel(), _ptr(r["flags"]), _ptr(r["n_outliers"]),
+                             _ptr(r["outlier_idx"]), _ptr(r["Xq"]), _ptr(r["sX"]),
+                             _ptr(r["X_out"]), _ptr(r["acc"]), _stream(dev)))
     return r

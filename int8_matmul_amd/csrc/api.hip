@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "li8_internal.h"
@@ -19,6 +20,26 @@ static __device__ __align__(256) char scratch[LI8_NOALLOC_SCRATCH_BYTES];
 namespace {
 
 bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+// The stage export's conversions: the bit set to one byte per column, and
+// the gathered outlier values from their 16-column chunks (rank i of row t
+// at ((i / 16) * T + t) * 16 + i % 16) to rows of stride K.
+__global__ void k_stage_flags_xo(const uint32_t *__restrict__ bits, const int32_t *__restrict__ meta,
+                                 const uint16_t *__restrict__ XO, int T, int K,
+                                 uint8_t *__restrict__ flags, uint16_t *__restrict__ xo_rows)
+{
+    const int nO = min(max(meta[0], 0), K);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (flags)
+        for (int64_t j = first; j < K; j += stride)
+            flags[j] = (uint8_t)((bits[j >> 5] >> (j & 31)) & 1u);
+    if (xo_rows)
+        for (int64_t e = first; e < (int64_t)T * nO; e += stride) {
+            const int64_t t = e / nO, i = e - t * nO;
+            xo_rows[t * K + i] = XO[((i >> 4) * T + t) * 16 + (i & 15)];
+        }
+}
 
 li8_status check_shape(int64_t T, int64_t K, int64_t N)
 {
@@ -641,6 +662,41 @@ li8_status llm_int8_export_stages(const void *workspace, size_t workspace_bytes,
             return LI8_ERR_HIP;
     }
     return LI8_OK;
+}
+
+li8_status llm_int8_stages(const void *X, const int8_t *Wq, const float *sW, float threshold,
+                           int64_t T, int64_t K, int64_t N, void *Y, void *workspace,
+                           size_t workspace_bytes, uint8_t *flags, int32_t *n_outliers,
+                           int32_t *outlier_idx, int8_t *Xq, float *sX, void *X_out, int32_t *acc,
+                           hipStream_t stream)
+{
+    // every check before anything is enqueued
+    li8_status st =
+        check_linear_args(X, Wq, threshold, T, K, N, workspace, workspace_bytes, WS_I8);
+    if (st == LI8_OK)
+        st = check_gemm_args(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes, WS_I8);
+    if (st == LI8_OK && (misaligned(Xq) || misaligned(sX) || misaligned(X_out)))
+        st = LI8_ERR_ALIGN;
+    if (st != LI8_OK || T == 0 || N == 0)
+        return st;
+    st = llm_int8_prepare(X, Wq, threshold, T, K, N, workspace, workspace_bytes, stream);
+    if (st == LI8_OK)
+        st = llm_int8_gemm(Wq, sW, T, K, N, Y, acc, workspace, workspace_bytes, stream);
+    if (st == LI8_OK)
+        st = llm_int8_export_stages(workspace, workspace_bytes, T, K, N, nullptr, n_outliers,
+                                    outlier_idx, Xq, sX, nullptr, stream);
+    if (st != LI8_OK || K == 0 || (!flags && !X_out))
+        return st;
+    const WsLayout L = ws_layout(T, K, N);
+    const char *ws = static_cast<const char *>(workspace);
+    const int64_t work = std::max<int64_t>(K, T * K);
+    const unsigned blocks = (unsigned)std::min<int64_t>((work + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_stage_flags_xo, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint32_t *>(ws + L.bits),
+                       reinterpret_cast<const int32_t *>(ws + L.meta),
+                       reinterpret_cast<const uint16_t *>(ws + L.XO), (int)T, (int)K, flags,
+                       static_cast<uint16_t *>(X_out));
+    return from_hip(hipGetLastError());
 }
 
 } // extern "C"

@@ -42,6 +42,7 @@ def test_header_declares_the_expected_entry_points():
         "li8_status_str", "int8_quantize_weight", "llm_int8_workspace_bytes",
         "llm_int8_linear_workspace_bytes", "llm_int8_plan", "llm_int8_linear_noalloc",
         "llm_int8_linear", "llm_int8_prepare", "llm_int8_gemm", "llm_int8_export_stages",
+        "llm_int8_stages",
         "llm_int8_linear_fp16w", "llm_int8_prepare_fp16w", "llm_int8_gemm_fp16w",
         "smoothquant_column_absmax", "smoothquant_factors", "smoothquant_quantize_weight",
         "smoothquant_prepare", "smoothquant_linear",
@@ -206,6 +207,19 @@ def test_prepare_and_gemm_validation(lib):
     e = lib.llm_int8_export_stages
     assert e(None, 0, 32, 64, 48, None, None, None, None, None, None, None) == WORKSPACE
     assert e(P, need, 32, 65, 48, None, None, None, None, None, None, None) == SHAPE
+    # the whole-call stage export checks everything before enqueueing anything
+    s = lib.llm_int8_stages
+    outs = (P, P, P, P, P, P, P)   # flags, nO, idx, Xq, sX, X_out, acc
+    assert s(None, P, P, 6.0, 32, 64, 48, P2, P, need, *outs, None) == INVALID
+    assert s(P, P, None, 6.0, 32, 64, 48, P2, P, need, *outs, None) == INVALID
+    assert s(P, P, P, math.nan, 32, 64, 48, P2, P, need, *outs, None) == INVALID
+    assert s(P, P, P, 6.0, 32, 64, 48, None, P, need, *outs, None) == INVALID
+    assert s(P, P, P, 6.0, 32, 72, 48, P2, P, need, *outs, None) == SHAPE
+    assert s(P, P, P, 6.0, 32, 64, 48, P2, P, need8 - 1, *outs, None) == WORKSPACE
+    assert s(P, P, P, 6.0, 32, 64, 48, P2, P, need, P, P, P, MIS, P, P, P, None) == ALIGN
+    assert s(P, P, P, 6.0, 32, 64, 48, P2, P, need, P, P, P, P, P, MIS, P, None) == ALIGN
+    assert s(P, P, P, 6.0, 32, 64, 48, P2, P, need, P, P, P, P, P, P, MIS, None) == ALIGN
+    assert s(P, P, P, 6.0, 0, 64, 48, P2, P, need, *outs, None) == OK   # empty call
 
 
 def test_fp16w_validation(lib):

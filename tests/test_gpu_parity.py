@@ -506,3 +506,38 @@ def test_long_prompt_special_rows():
     g, o = check_full(X, W, 6.0, "long prompt, zero-scale rows, 300 outlier columns")
     assert o["nO"] == 300
     assert g["sX"][3] == 0 and g["sX"][2049] == 0
+
+
+# ---------------------------------------------------------------------------
+# llm_int8_stages: every intermediate result of one call, on each path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,K,N", [
+    (300, 272, 520),     # tiled path
+    (8, 4096, 300),      # few tokens (two-call route of the fused kernel)
+    (8, 11008, 300),     # few tokens, long K (split-K route)
+    (2050, 1024, 96),    # one wave per token row in the prepare kernel
+])
+@pytest.mark.parametrize("thr", [6.0, np.inf, 0.0])
+def test_stages_entry_point(T, K, N, thr):
+    say(f"case stages {T}x{K}x{N} thr={thr}")
+    w = workloads.WORKLOADS["ffn_13b"]
+    rng = np.random.default_rng(T * 3 + K * 5 + N * 7)
+    X, _ = workloads.make_activation(w, seed=int(rng.integers(1 << 30)), T=T, K=K)
+    W = workloads.make_weight(w, seed=int(rng.integers(1 << 30)), N=N, K=K)
+    Xd = dev(X)
+    Wq, sW = li8.quantize_weight(dev(W))
+    r = {k: host(v) for k, v in li8.stages(Xd, Wq, sW, thr).items()}
+    Yl = host(li8.linear(Xd, Wq, sW, thr))
+    o = oracle.linear(X, host(Wq), host(sW), thr, stages=True)
+    nO = int(r["n_outliers"][0])
+    assert nO == o["nO"], "outlier count"
+    assert np.array_equal(r["flags"][:K], o["flags"]), "outlier flags"
+    assert np.array_equal(r["outlier_idx"][:nO], o["idx"]), "outlier index list"
+    assert np.array_equal(r["Xq"], o["Xq"]), "token codes"
+    assert np.array_equal(r["sX"][:T], o["sX"]), "token scales"
+    assert np.array_equal(r["X_out"][:, :nO], X[:, o["idx"]]), "gathered outlier values"
+    assert np.array_equal(r["acc"], o["acc"]), "int32 accumulators"
+    assert np.array_equal(r["Y"].view(np.uint16), Yl.view(np.uint16)), "stages and linear differ"
+    e = rel_err(r["Y"], o["Y"])
+    assert e <= TOL, f"fp16 output error {e}"
