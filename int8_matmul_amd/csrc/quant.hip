@@ -658,8 +658,8 @@ __global__ __launch_bounds__(kThreads) void k_prepare_rows(
         uint32_t anym = 0;
 #pragma unroll
         for (int s = 0; s < CH; s++) {
-            const int c = lane + 64 * s;
-            skipm[s] = c < nchunk ? (bits[c >> 2] >> (8 * (c & 3))) & 0xffu : 0u;
+            const int c = lane + 64 * s, cc = min(c, nchunk - 1);   // (a read inside the bit set either way)
+            skipm[s] = c < nchunk ? (bits[cc >> 2] >> (8 * (c & 3))) & 0xffu : 0u;
             anym |= (__ballot(skipm[s] != 0u) != 0ull ? 1u : 0u) << s;
         }
         anym = __builtin_amdgcn_readfirstlane(anym);
