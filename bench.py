@@ -73,6 +73,10 @@ def parse():
                     help="skip timing the vendor int8 GEMM (torch._int_mm) for reference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--power-seconds", type=float, default=0.0,
+                    help="after the measurements, replay graphs of the whole call and of the "
+                         "GEMM alone for this long each while `amd-smi metric --power --clock` "
+                         "is sampled, and report socket power and XCD clocks (0: skip)")
     return ap.parse_args()
 
 
@@ -131,6 +135,54 @@ def clock_adjusted(path_src: str, workload: str, shape, achieved: float):
     return {"sclk_ghz": ghz, "peak": round(peak, 1), "frac": round(achieved / peak, 4),
             "sclk_from": f"profiles/{name}.json: SQ_BUSY_CYCLES per shader engine over the "
                          "profiled k_gemm launches (the 5.0 POP/s peak assumes 2.4 GHz)"}
+
+
+def power_samples(g, seconds: float) -> dict:
+    """Replays graph g back to back for `seconds` while a thread samples
+    `amd-smi metric --power --clock --json` every 0.25 s; returns the medians
+    (over the samples after the first second) of the socket power and of the
+    GFX clock averaged over the XCDs."""
+    import statistics
+    import subprocess
+    import threading
+
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            t = time.perf_counter()
+            try:
+                r = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"],
+                                   capture_output=True, text=True, timeout=5)
+                d = json.loads(r.stdout)
+                gd = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                clk = [v["clk"]["value"] for k, v in gd["clock"].items() if k.startswith("gfx_")]
+                samples.append((t, float(gd["power"]["socket_power"]["value"]),
+                                sum(clk) / len(clk)))
+            except Exception as e:   # amd-smi missing or its format differs
+                samples.append((t, None, repr(e)[:120]))
+            time.sleep(0.25)
+
+    th = threading.Thread(target=sampler)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        g.replay()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    good = [x for x in samples if x[1] is not None and x[0] - t0 > 1.0]
+    if not good:
+        return {"error": samples[-1][2] if samples else "no sample"}
+    return {"socket_power_w": statistics.median(x[1] for x in good),
+            "gfx_clock_mhz": round(statistics.median(x[2] for x in good), 1),
+            "samples": len(good)}
 
 
 def cpu_baseline(X, W, w, target_s: float, variant: str, thr: float):
@@ -423,6 +475,18 @@ def main():
     prep_ms = graph_ms(g_prep)
     del g_prep
 
+    power = None
+    if args.power_seconds > 0:
+        for b in sets:
+            prep(b)
+        torch.cuda.synchronize()
+        power = {"what": "amd-smi metric --power --clock every 0.25 s during back-to-back graph "
+                         "replays; medians over the samples after the first second: socket power, "
+                         "and the mean over the 8 XCDs of the GFX clock",
+                 "call": power_samples(capture(call, R, nsets), args.power_seconds)}
+        if not few:
+            power["gemm"] = power_samples(capture(gemm, R, nsets), args.power_seconds)
+
     st = li8.export_stages(ws, T, K, N)
     nO = int(st["n_outliers"].cpu()[0])
     nO16 = (nO + 15) // 16 * 16
@@ -580,6 +644,8 @@ def main():
         "vendor_int8_gemm": reference,
         "roofline": roofline,
     }
+    if power is not None:
+        out["power"] = power
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(X_np, W_np, w, args.cpu_seconds, args.variant, thr)
     else:
