@@ -10,9 +10,11 @@
 //   weight scale     sW[n] = max_k |W[n,k]| / 127, codes likewise.
 // Scales are fp32 (IEEE division), codes round half to even.
 //
-// All three kernels are HBM-bound streaming passes: 16-byte coalesced
-// loads, the row or column-strip reduction kept in registers, wave-level
-// reductions, and a single atomic per 32 columns for the outlier bit set.
+// The weight quantization, the detection and the token quantization
+// kernels are HBM-bound streaming passes: 16-byte coalesced loads, the row
+// or column-strip reduction kept in registers, wave-level reductions, and
+// the outlier bit set written as per-strip partial words with plain stores
+// (no atomics on global memory).
 //
 // Magnitudes are compared as integers: for a finite binary16 value h,
 // |h| is monotone in (h & 0x7fff), so |x| > thr  <=>  (h & 0x7fff) > H,
