@@ -478,6 +478,8 @@ def test_many_tokens_narrow():
     (2050, 272, 520),    # 34 chunks per row: most lanes hold none; last workgroup half past T
     (8201, 1040, 48),    # 2051 workgroups of rows, the last with one live wave
     (4096, 8192, 32),    # the 70B slice's K
+    (2049, 16, 40),      # one bit-set word, two chunks per row
+    (2048, 4080, 24),    # the last bit-set word half used
 ])
 @pytest.mark.parametrize("thr", [6.0, np.inf, 0.0])
 def test_long_prompt_rows(T, K, N, thr):
