@@ -274,7 +274,9 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer "
-              "runs on a single MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "runs on a single MI355X. Across GPUs it would be split by output features "
+              "(each GPU its share of Wq and sW, X replicated), which is not built here.",
+              file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
