@@ -357,6 +357,7 @@ def test_determinism_and_canary():
 @pytest.mark.parametrize("T,K,N", [
     (300, 1040, 520),     # tiled path, few detection strips
     (4096, 512, 300),     # tiled path, all 16 detection strips
+    (2050, 1040, 300),    # one wave per token row, the last workgroup half past T
     (8, 4096, 300),       # few tokens (prepare + gemm route)
     (8, 11008, 300),      # few tokens, split K (prepare + gemm route)
 ])
